@@ -1,0 +1,318 @@
+"""Benchmark of prefix-shared attention forward on one MI355X.
+
+Headline workload (the step timed K times): the GRPO flat-packed forward,
+P=2048 shared prompt + 8 rollouts x 512 tokens, Hq=32, Hkv=8, D=128, bf16 --
+planner, prefix pass, own-rollout diagonal and epilogue in one launch.
+``value`` is useful TFLOP/s: 4*D*Hq per visible (query row, key) pair,
+masked pairs and softmax excluded.
+
+In the same run the verify path (paged split-KV pass + log-sum-exp combine)
+is timed on 8 requests x 16384 prefix tokens, Lx=4, Hq=32, Hkv=8, D=128,
+bf16 ("verify us @16k", with its HBM GB/s against the algorithmic bytes that
+count every prefix K/V byte once), and, with --all, the fp8 verify and the
+large ragged GRPO workloads.
+
+Every timed call is preceded (outside the timed events) by a 1 GiB write that
+evicts L2 and the 256 MiB MALL, so every K/V byte is read from HBM.
+Correctness against the float64 oracle is checked before timing.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "useful TFLOP/s + HBM GB/s (% roofline) of prefix-shared attn fwd; verify µs @16k"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+FLUSH_BYTES = 1 << 30
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ work counts
+def flat_visible_pairs(inst) -> int:
+    p = inst.prefix_len
+    s = inst.seg_lens.astype(np.int64)
+    return int(p * (p + 1) // 2 + np.sum(s * p + s * (s + 1) // 2))
+
+
+def flat_useful_flops(inst) -> float:
+    return 4.0 * inst.d * inst.hq * flat_visible_pairs(inst)
+
+
+def flat_alg_bytes(inst) -> float:
+    es = 4 if inst.dtype == 0 else 2
+    t = inst.total_tokens
+    return float(t * inst.hq * inst.d * 2 * es + 2 * t * inst.hkv * inst.d * es + 4 * t * inst.hq
+                 + 4 * (inst.num_segments + 1))
+
+
+def paged_useful_flops(inst) -> float:
+    lx = inst.draft_len
+    pl = inst.prefix_lens.astype(np.int64)
+    return 4.0 * inst.d * inst.hq * float(np.sum(lx * pl + lx * (lx + 1) // 2))
+
+
+def paged_alg_bytes(inst) -> float:
+    bkv = {0: 4, 1: 2, 2: 1}[inst.kv_dtype]
+    bq = 4 if inst.q_dtype == 0 else 2
+    b, lx = inst.batch, inst.draft_len
+    pl = inst.prefix_lens.astype(np.int64)
+    n_pages = int(inst.kv_indptr[-1])
+    return float(np.sum(2 * pl * inst.hkv * inst.d * bkv) + b * lx * inst.hq * inst.d * 2 * bq
+                 + 2 * b * lx * inst.hkv * inst.d * bkv + 4 * b * lx * inst.hq
+                 + 4 * (n_pages + 2 * b + 1))
+
+
+# ------------------------------------------------------------------ runners
+class FlatRunner:
+    def __init__(self, ps, inst):
+        import torch
+        from gpu_util import to_dev
+
+        self.ps, self.inst = ps, inst
+        self.q = to_dev(inst.q, inst.dtype)
+        self.k = to_dev(inst.k, inst.dtype)
+        self.v = to_dev(inst.v, inst.dtype)
+        self.seg = torch.from_numpy(inst.seg_offsets).cuda()
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.ps.fwd_flat(self.q, self.k, self.v, self.inst.prefix_len, self.seg, self.inst.max_seg_len,
+                         sm_scale=self.inst.sm_scale, out=self.o, lse=self.lse)
+
+    def check(self, rows):
+        import torch
+        from gpu_util import compare, to_f64
+        from oracle.attention import attn_flat
+
+        self()
+        torch.cuda.synchronize()
+        inst = self.inst
+        ro, rl = attn_flat(inst.q, inst.k, inst.v, inst.prefix_len, inst.seg_offsets, inst.sm_scale,
+                           dtype=inst.dtype, rows=rows)
+        return compare(to_f64(self.o)[rows], to_f64(self.lse)[rows], ro, rl, "bf16", inst.name)
+
+
+class PagedRunner:
+    def __init__(self, ps, inst):
+        import torch
+        from gpu_util import to_dev
+
+        self.ps, self.inst = ps, inst
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        self.q = to_dev(inst.q, inst.q_dtype)
+        self.kp = to_dev(inst.k_pool, inst.kv_dtype)
+        self.vp = to_dev(inst.v_pool, inst.kv_dtype)
+        self.kx = to_dev(inst.k_ext, inst.kv_dtype)
+        self.vx = to_dev(inst.v_ext, inst.kv_dtype)
+        self.indptr, self.indices, self.plens = i32(inst.kv_indptr), i32(inst.kv_indices), i32(inst.prefix_lens)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+        desc = ps.paged_desc(inst.batch, inst.draft_len, 16, inst.num_pages, self.plens.data_ptr(),
+                             self.indptr.data_ptr(), self.indices.data_ptr(), inst.max_prefix_len,
+                             self.kx.data_ptr(), self.vx.data_ptr())
+        nbytes = ps.psattn_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        self.info = ps.plan_info(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
+
+    def __call__(self):
+        i = self.inst
+        self.ps.fwd_paged(self.q, self.kp, self.vp, self.indptr, self.indices, self.plens, self.kx, self.vx,
+                          i.draft_len, i.max_prefix_len, sm_scale=i.sm_scale, k_scale=i.k_scale,
+                          v_scale=i.v_scale, kv_dtype=i.kv_dtype, out=self.o, lse=self.lse, workspace=self.ws)
+
+    def check(self):
+        import torch
+        from gpu_util import compare, kind_of, to_f64
+        from oracle.attention import attn_paged
+
+        self()
+        torch.cuda.synchronize()
+        i = self.inst
+        reqs = [0, i.batch - 1]
+        ro, rl = attn_paged(i.q, i.k_pool, i.v_pool, i.kv_indptr, i.kv_indices, i.prefix_lens, i.k_ext,
+                            i.v_ext, i.draft_len, i.sm_scale, k_scale=i.k_scale, v_scale=i.v_scale,
+                            q_dtype=i.q_dtype, kv_dtype=i.kv_dtype, requests=reqs)
+        sel = np.concatenate([np.arange(b * i.draft_len, (b + 1) * i.draft_len) for b in reqs])
+        return compare(to_f64(self.o)[sel], to_f64(self.lse)[sel], ro[sel], rl[sel],
+                       kind_of(i.q_dtype, i.kv_dtype), i.name)
+
+
+def time_calls(fn, flush, steps: int, warmup: int):
+    """Median-free plain timing: mean, min and p50 of per-call event times (ms),
+    each call preceded by a cache-evicting write outside the events."""
+    import torch
+
+    for _ in range(warmup):
+        flush.zero_()
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.zero_()
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    return dict(mean=float(ms.mean()), min=float(ms.min()), p50=float(np.median(ms)), wall_s=wall)
+
+
+def cpu_baseline(inst, flops_fn):
+    """The float64 oracle on the host cores, on the whole GRPO workload."""
+    from oracle.attention import attn_flat
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    attn_flat(inst.q, inst.k, inst.v, inst.prefix_len, inst.seg_offsets, inst.sm_scale, dtype=inst.dtype)
+    dt = time.perf_counter() - t0
+    return {"value": flops_fn(inst) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole {inst.name} workload ({inst.total_tokens} rows x {inst.hq} heads), "
+                      f"float64 build_kv expansion, {dt:.2f} s"}
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    src = os.path.join(ROOT, "prefix_shared_block_amd", "csrc", "psattn_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if prof.get("kernel_source_sha256") != h:
+        return None
+    return prof.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--all", action="store_true", help="also time the fp8 verify and ragged GRPO workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from prefix_shared_block_amd import psattn as ps
+    from psattn_inputs import make_config
+
+    ps.load()
+    torch.cuda.set_device(0)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    log("generating grpo workload")
+    g_inst = make_config("grpo")
+    grpo = FlatRunner(ps, g_inst)
+    if not args.no_check:
+        from gpu_util import sample_rows
+
+        grpo.check(sample_rows(g_inst))
+    log("timing grpo")
+    tg = time_calls(grpo, flush, args.steps, args.warmup)
+    g_flops = flat_useful_flops(g_inst)
+    g_tflops = g_flops / (tg["mean"] * 1e-3) / 1e12
+    g_tflops_best = g_flops / (tg["min"] * 1e-3) / 1e12
+    traffic = traffic_from_profile("flat_fwd", "grpo")
+    out = {
+        "metric": METRIC,
+        "value": round(g_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tg["mean"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "grpo: P=2048 + 8 rollouts x 512, Hq=32, Hkv=8, D=128, bf16 N(0,1), flat packed",
+                   "global_batch": 8, "seq_len": 2048 + 512, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "flat_fwd_kernel<128,bf16>",
+                     "per_launch_useful_flop": g_flops, "best_call_tflops": round(g_tflops_best, 2)},
+        "grpo_hbm_gbs": round(flat_alg_bytes(g_inst) / (tg["mean"] * 1e-3) / 1e9, 1),
+    }
+    del grpo
+
+    log("generating verify16k workload")
+    v_inst = make_config("verify16k")
+    ver = PagedRunner(ps, v_inst)
+    if not args.no_check:
+        ver.check()
+    log("timing verify16k")
+    tv = time_calls(ver, flush, args.steps, args.warmup)
+    vb = paged_alg_bytes(v_inst)
+    v_gbs = vb / (tv["mean"] * 1e-3) / 1e9
+    out["verify16k"] = {"us": round(tv["mean"] * 1e3, 2), "us_min": round(tv["min"] * 1e3, 2),
+                        "hbm_gbs": round(v_gbs, 1), "frac_hbm": round(v_gbs / PEAK_HBM_GBS, 4),
+                        "alg_bytes": vb, "useful_tflops": round(paged_useful_flops(v_inst) / (tv["mean"] * 1e-3) / 1e12, 2),
+                        "n_splits": ver.info.n_splits, "split_len": ver.info.split_len}
+    del ver
+
+    if args.all:
+        log("generating verify_fp8 workload")
+        f_inst = make_config("verify_fp8")
+        fr = PagedRunner(ps, f_inst)
+        if not args.no_check:
+            fr.check()
+        tf = time_calls(fr, flush, args.steps, args.warmup)
+        fb = paged_alg_bytes(f_inst)
+        out["verify_fp8"] = {"us": round(tf["mean"] * 1e3, 2), "hbm_gbs": round(fb / (tf["mean"] * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(fb / (tf["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                             "n_splits": fr.info.n_splits}
+        del fr
+        log("generating grpo_ragged workload")
+        r_inst = make_config("grpo_ragged")
+        rr = FlatRunner(ps, r_inst)
+        if not args.no_check:
+            from gpu_util import sample_rows
+
+            rr.check(sample_rows(r_inst, n_random=8))
+        tr = time_calls(rr, flush, max(5, args.steps // 3), 2)
+        rf = flat_useful_flops(r_inst)
+        out["grpo_ragged"] = {"ms": round(tr["mean"], 4), "useful_tflops": round(rf / (tr["mean"] * 1e-3) / 1e12, 2),
+                              "frac_mfma": round(rf / (tr["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del rr
+
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu baseline)")
+        out["cpu_baseline"] = cpu_baseline(g_inst, flat_useful_flops)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * psattn.h -- prefix-shared attention forward for AMD gfx950 (MI355X).
+ *
+ * C ABI of libpsattn.so.  Plain pointers and sizes only.  Unless stated
+ * otherwise a pointer is a DEVICE pointer; the library never frees, keeps or
+ * allocates caller memory.
+ *
+ * What is computed.  PrefixSharing PR #50 ("设计简介", design summary) packs
+ * a shared prompt P and N rollout suffixes flat as [P | S1 | ... | SN], keeps
+ * the prefix K/V once, and controls visibility with a block-causal mask
+ * instead of copying the prefix into every rollout (the build_kv route); the
+ * result is stated to be exactly that of ordinary causal attention over each
+ * expanded sequence [P | Si].  Row r of the packed buffer sees key c iff
+ * c <= r and (c < P or c lies in r's own segment).  sglang PR #27382
+ * ("实现拆解", implementation breakdown) applies the same idea to EAGLE
+ * target-verify: a few draft rows per request read the request's long paged
+ * prefix in splits (one partial O and log-sum-exp per split), and a second
+ * stage merges the splits by log-sum-exp together with the small causal
+ * draft-by-draft block.
+ *
+ * For every query row r and query head h (kv head g = h / (Hq / Hkv)):
+ *     z_c  = sm_scale * <q[r,h,:], K[c,g,:]>      over the keys c that r sees
+ *     lse  = ln sum_c exp(z_c)                     (natural log, fp32)
+ *     o    = sum_c exp(z_c - lse) * V[c,g,:]       (stored in q's dtype)
+ * with K, V multiplied by k_scale, v_scale in paged mode.
+ *
+ * Execution.  All work is enqueued asynchronously on the caller's stream
+ * (a hipStream_t passed as void*, NULL = the null stream).  Nothing is read
+ * back from the device: every size the launch needs comes in as a host
+ * scalar.  All arguments are validated on the host before the first launch,
+ * so an error status means nothing was enqueued and no output was touched.
+ * Faults inside kernels (for example a device array that breaks the
+ * documented invariants) surface as HIP errors at the caller's next
+ * synchronisation.  The library keeps no mutable global state apart from a
+ * per-thread last-error string.
+ */
+#ifndef PSATTN_H_
+#define PSATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element storage types. */
+typedef enum {
+  PSATTN_F32 = 0,       /* IEEE binary32 */
+  PSATTN_BF16 = 1,      /* bfloat16 */
+  PSATTN_FP8_E4M3 = 2   /* OCP fp8 e4m3fn (bias 7, no inf, max 448) */
+} psattn_dtype;
+
+typedef enum {
+  PSATTN_OK = 0,
+  PSATTN_E_INVAL = 1,        /* malformed argument (null, negative, misaligned, inconsistent) */
+  PSATTN_E_UNSUPPORTED = 2,  /* well-formed but outside the supported set (no fallback is run) */
+  PSATTN_E_WORKSPACE = 3,    /* workspace missing or smaller than psattn_workspace_size() */
+  PSATTN_E_HIP = 4           /* a HIP runtime call failed while enqueuing */
+} psattn_status;
+
+enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
+
+/*
+ * Segment descriptor.  Device arrays are borrowed until the enqueued work
+ * has finished.
+ *
+ * Flat mode (GRPO rollouts sharing one prompt):
+ *   q, o      [total_tokens, Hq, D]  row-major, packed [P | S1 | ... | SN]
+ *   k, v      [total_tokens, Hkv, D]
+ *   lse       [total_tokens, Hq]     fp32
+ *   seg_offsets (device, int32, num_segments + 1 entries): seg_offsets[0] =
+ *     prefix_len, seg_offsets[num_segments] = total_tokens, non-decreasing.
+ *     Empty segments are allowed.  num_segments = 0 means the buffer holds the
+ *     prefix alone (then total_tokens == prefix_len and seg_offsets may be NULL).
+ *   max_seg_len (host): an upper bound of every segment length; it is only
+ *     used for validation of sizes, never for correctness.
+ *
+ * Paged mode (speculative target-verify, uniform draft length):
+ *   q, o      [batch * draft_len, Hq, D]; draft row t of request b is row
+ *             b * draft_len + t and sits at position prefix_lens[b] + t.
+ *   lse       [batch * draft_len, Hq]   fp32
+ *   k, v      page pools [num_pages, page_size, Hkv, D] in kv dtype
+ *   kv_indptr (device, int32, batch + 1): request b owns the page ids
+ *             kv_indices[kv_indptr[b] .. kv_indptr[b+1]); prefix token t of b
+ *             is slot t % page_size of page kv_indices[kv_indptr[b] + t / page_size].
+ *             kv_indptr[b+1] - kv_indptr[b] >= ceil(prefix_lens[b] / page_size).
+ *   prefix_lens (device, int32, batch): 0 <= prefix_lens[b] <= max_prefix_len.
+ *   max_prefix_len (host): upper bound of prefix_lens (sizes the split grid).
+ *   k_ext, v_ext [batch * draft_len, Hkv, D] in kv dtype: the draft block's own
+ *             K/V; draft row t sees draft keys 0..t.
+ */
+typedef struct {
+  int32_t mode;
+  /* flat */
+  int64_t total_tokens;
+  int32_t prefix_len;
+  int32_t num_segments;
+  const int32_t* seg_offsets;
+  int32_t max_seg_len;
+  /* paged */
+  int32_t batch;
+  int32_t draft_len;
+  int32_t page_size;
+  int32_t num_pages;
+  const int32_t* prefix_lens;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  int32_t max_prefix_len;
+  const void* k_ext;
+  const void* v_ext;
+} psattn_desc;
+
+/*
+ * Launch plan summary (host struct) reported by psattn_plan_dump /
+ * psattn_plan_host.  n_items is the number of workgroups the forward launch
+ * of the prefix pass uses (one work item each, idle ones included).
+ */
+typedef struct {
+  int64_t n_items;
+  int32_t tile_tokens;     /* flat: query tokens per tile (rows per tile / G) */
+  int32_t rows_per_tile;   /* stacked query rows (tokens x GQA heads) per workgroup */
+  int32_t n_splits;        /* paged: splits per (request, kv head) */
+  int32_t split_len;       /* paged: prefix tokens per split (multiple of page_size) */
+  int32_t kv_tile;         /* keys per inner-loop tile */
+  int32_t reserved;
+} psattn_plan_info;
+
+/* Work-item record written by the planner: 10 int32 per item, in this order. */
+enum {
+  PSATTN_ITEM_FIELDS = 10,
+  PSATTN_ITEM_NONE = 0,        /* idle workgroup */
+  PSATTN_ITEM_FLAT_PREFIX = 1, /* tile of prefix rows */
+  PSATTN_ITEM_FLAT_SUFFIX = 2, /* tile of one rollout's rows */
+  PSATTN_ITEM_PAGED_SPLIT = 3  /* one split of one request's prefix, one kv head */
+};
+/* fields: kind, h_kv, seg (flat: rollout index or -1; paged: request),
+ *         q_begin, q_end (flat: packed rows; paged: draft rows 0..draft_len),
+ *         r0_begin, r0_end, r1_begin, r1_end (key ranges; a flat row r sees
+ *         (r0 U r1) intersected with [0, r]; a paged split covers prefix keys r0),
+ *         split. */
+
+/*
+ * Bytes of scratch the forward call needs for this descriptor (0 in flat
+ * mode; paged mode: per-split partial O and LSE in fp32).  Host only; does
+ * not touch the GPU.  Returns 0 and sets the last error on invalid input.
+ */
+size_t psattn_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                             psattn_dtype q_dtype, psattn_dtype kv_dtype);
+
+/*
+ * Forward pass (flat: one launch; paged: split pass + combine pass).
+ *   q, k, v, o, lse : device pointers, 16-byte aligned, layouts as above.
+ *   hq, hkv, d      : heads and head dim; hq % hkv == 0; d in {64, 128, 256}.
+ *   sm_scale        : logit scale (> 0), e.g. 1/sqrt(d).
+ *   q_dtype/kv_dtype: supported pairs (F32,F32) and (BF16,BF16) in both modes,
+ *                     (BF16,FP8_E4M3) in paged mode. o has q's dtype.
+ *   k_scale,v_scale : per-tensor multipliers of stored K and V (paged mode;
+ *                     must be 1 in flat mode).
+ *   workspace       : device scratch of at least psattn_workspace_size() bytes
+ *                     (may be NULL when that size is 0), 256-byte aligned.
+ *   stream          : hipStream_t.
+ * Returns PSATTN_OK once the work is enqueued.
+ */
+psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                         float sm_scale, psattn_dtype q_dtype, psattn_dtype kv_dtype,
+                         float k_scale, float v_scale, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Test hook: run the segment planner ON THE DEVICE for every workgroup of the
+ * prefix-pass launch psattn_fwd would make and write its work items
+ * (PSATTN_ITEM_FIELDS int32 each, in workgroup order) to items_dev, which
+ * must hold `capacity` items.  info_host (host) receives the plan summary.
+ * With items_dev == NULL only info_host is filled (no GPU work).
+ */
+psattn_status psattn_plan_dump(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                               psattn_dtype q_dtype, psattn_dtype kv_dtype, int32_t* items_dev,
+                               int64_t capacity, psattn_plan_info* info_host, void* stream);
+
+/*
+ * Same planner code run on the host: the descriptor's arrays (seg_offsets,
+ * prefix_lens) are HOST pointers here and items_host is a host buffer.
+ */
+psattn_status psattn_plan_host(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                               psattn_dtype q_dtype, psattn_dtype kv_dtype, int32_t* items_host,
+                               int64_t capacity, psattn_plan_info* info_host);
+
+/* Static description of a status code. */
+const char* psattn_status_string(psattn_status status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* psattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PSATTN_H_ */

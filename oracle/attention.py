@@ -96,38 +96,39 @@ def attn_flat(q, k, v, prefix_len: int, seg_offsets: Sequence[int], sm_scale: fl
     agreement).  With N = 0 the buffer is the prefix alone, an expansion with
     an empty suffix.
     """
-    qf = q if dtype is None else decode(q, dtype)
-    kf = k if dtype is None else decode(k, dtype)
-    vf = v if dtype is None else decode(v, dtype)
+    def dec(x):
+        # decoding is elementwise and exact, so gathering first is the same
+        return x if dtype is None else decode(x, dtype)
+
     offs = [int(x) for x in seg_offsets]
-    t_n = qf.shape[0]
+    t_n = q.shape[0]
     p = int(prefix_len)
     n = len(offs) - 1
     if offs[0] != p or offs[-1] != t_n or any(b < a for a, b in zip(offs, offs[1:])):
         raise ValueError("bad seg_offsets")
-    hq, d = qf.shape[1], qf.shape[2]
+    hq, d = q.shape[1], q.shape[2]
     want = np.arange(t_n) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.full((want.size, hq, d), np.nan)
     lse = np.full((want.size, hq), np.nan)
     where = {int(r): i for i, r in enumerate(want)}
 
     segs = [(offs[i], offs[i + 1]) for i in range(n)] if n > 0 else [(p, p)]
-    pre_rows = [r for r in want if r < p]
+    pre_rows = [int(r) for r in want if r < p]
     for si, (a, b) in enumerate(segs):
-        kx = build_kv(kf, p, a, b)
-        vx = build_kv(vf, p, a, b)
-        qx = build_kv(qf, p, a, b)
-        sel = [r for r in want if a <= r < b]
-        if si == 0 or check_prefix:
-            sel_pre = pre_rows
-        else:
-            sel_pre = []
-        local = np.array([r for r in sel_pre] + [p + (r - a) for r in sel], dtype=np.int64)
-        if local.size == 0:
+        sel = [int(r) for r in want if a <= r < b]
+        sel_pre = pre_rows if (si == 0 or check_prefix) else []
+        flat_rows = list(sel_pre) + list(sel)
+        if not flat_rows:
             continue
-        oo, ll = causal_attention(qx[local], local, kx, vx, sm_scale)
-        for j, r in enumerate(list(sel_pre) + list(sel)):
-            slot = where[int(r)]
+        kx = dec(build_kv(k, p, a, b))
+        vx = dec(build_kv(v, p, a, b))
+        # query rows of the expanded sequence [P | S_i]: prefix row r stays at
+        # r, suffix row r moves to P + (r - o_i)
+        local = np.array(list(sel_pre) + [p + (r - a) for r in sel], dtype=np.int64)
+        qr = dec(q[np.asarray(flat_rows, dtype=np.int64)])
+        oo, ll = causal_attention(qr, local, kx, vx, sm_scale)
+        for j, r in enumerate(flat_rows):
+            slot = where[r]
             if r < p and si > 0:
                 if not (np.allclose(o[slot], oo[j], rtol=0, atol=1e-12)
                         and np.allclose(lse[slot], ll[j], rtol=0, atol=1e-12)):

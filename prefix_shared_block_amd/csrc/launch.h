@@ -1,0 +1,60 @@
+// launch.h -- internal interface between the C-ABI host code and the HIP
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace psattn {
+
+struct FlatArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seg_offsets;
+  int32_t prefix_len;
+  int32_t nseg;
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  int32_t tile_tokens;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct PagedArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const void* k_ext;
+  const void* v_ext;
+  void* o;
+  float* lse;
+  const int32_t* prefix_lens;
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  float* part_o;    // [B, Hkv, n_splits, R, D]  normalised partial outputs
+  float* part_lse;  // [B, Hkv, n_splits, R]     log2-domain partial LSE
+  int32_t batch;
+  int32_t draft_len;
+  int32_t page_size;
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  int32_t rows;  // draft_len * g
+  int32_t n_splits;
+  int32_t split_len;
+  float scale_log2;  // sm_scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// dtype codes follow psattn_dtype (0 f32, 1 bf16, 2 fp8 e4m3fn)
+int launch_flat(const FlatArgs& a, int d, int dtype, int64_t n_blocks, void* stream);
+int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, int row_blocks,
+                 int64_t n_blocks, void* stream);
+int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,
+                     int32_t* items, void* stream);
+const char* hip_error_string(int err);
+
+}  // namespace psattn

@@ -1,0 +1,226 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* the shared library loads and exports every function include/psattn.h declares;
+* argument validation returns the documented status before any HIP call;
+* the planner (same header code the kernels run) matches the independent
+  enumeration in oracle/plan.py bit-exactly, and its items cover exactly the
+  visible (row, key) pairs.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle.plan import coverage_flat, enumerate_flat, enumerate_paged
+from oracle.brute import visible
+from prefix_shared_block_amd import psattn as ps
+from psattn_inputs import make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ps.LIB_PATH):
+        from prefix_shared_block_amd.build import build
+
+        build()
+    return ps.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "psattn.h")).read()
+    names = set(re.findall(r"\b(psattn_[a-z_]+)\s*\(", hdr))
+    assert {"psattn_fwd", "psattn_workspace_size", "psattn_plan_dump", "psattn_plan_host",
+            "psattn_status_string", "psattn_last_error"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches_header(lib):
+    # offsets of the C struct (x86-64 SysV): int64 after int32 is 8-aligned
+    assert ctypes.sizeof(ps.PsattnDesc) == 104
+    assert ps.PsattnDesc.seg_offsets.offset == 24
+    assert ps.PsattnDesc.k_ext.offset == 88
+    assert ctypes.sizeof(ps.PsattnPlanInfo) == 32
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert ps.psattn_status_string(st)
+    assert "unknown" in ps.psattn_status_string(99)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _flat(t=96, p=64, n=2, offs=FAKE, mx=16):
+    return ps.flat_desc(t, p, n, offs, mx)
+
+
+def _call(desc, hq=2, hkv=2, d=64, qdt=ps.F32, kvdt=ps.F32, sm=0.125, ks=1.0, vs=1.0,
+          q=FAKE, o=FAKE, lse=FAKE, ws=0, wsb=0):
+    return ps.psattn_fwd(q, FAKE, FAKE, o, lse, desc, hq, hkv, d, sm, qdt, kvdt, ks, vs, ws, wsb, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=3, hkv=2), ps.E_INVAL),
+    (dict(hq=0), ps.E_INVAL),
+    (dict(d=96), ps.E_UNSUPPORTED),
+    (dict(qdt=ps.BF16, kvdt=ps.F32), ps.E_UNSUPPORTED),
+    (dict(qdt=ps.BF16, kvdt=ps.FP8), ps.E_UNSUPPORTED),  # fp8 K/V only in paged mode
+    (dict(qdt=7), ps.E_INVAL),
+    (dict(sm=0.0), ps.E_INVAL),
+    (dict(sm=float("nan")), ps.E_INVAL),
+    (dict(ks=2.0), ps.E_UNSUPPORTED),
+    (dict(q=0), ps.E_INVAL),
+    (dict(o=FAKE + 8), ps.E_INVAL),
+    (dict(lse=FAKE + 2), ps.E_INVAL),
+])
+def test_flat_validation(lib, kw, status):
+    assert _call(_flat(), **kw) == status
+    assert ps.psattn_last_error()
+
+
+@pytest.mark.parametrize("desc_kw,status", [
+    (dict(t=96, p=97), ps.E_INVAL),
+    (dict(t=-1), ps.E_INVAL),
+    (dict(n=-1), ps.E_INVAL),
+    (dict(n=0), ps.E_INVAL),           # T != P with no segments
+    (dict(offs=0), ps.E_INVAL),        # seg_offsets NULL
+    (dict(mx=8), ps.E_INVAL),          # N * max_seg_len < T - P
+])
+def test_flat_descriptor_validation(lib, desc_kw, status):
+    assert _call(_flat(**desc_kw)) == status
+
+
+def test_flat_gqa_group_too_large(lib):
+    assert _call(_flat(), hq=256, hkv=1) == ps.E_UNSUPPORTED
+
+
+def test_empty_inputs_enqueue_nothing(lib):
+    # T = 0 (and P = 0, N = 0): valid, nothing to do, no pointer is touched
+    assert _call(ps.flat_desc(0, 0, 0, 0, 0), q=0, o=0, lse=0) == ps.OK
+    d = ps.paged_desc(0, 4, 16, 0, 0, 0, 0, 0, 0, 0)
+    assert _call(d, qdt=ps.BF16, kvdt=ps.BF16, q=0, o=0, lse=0) == ps.OK
+
+
+def _paged(batch=2, lx=4, page=16, pages=64, mx=100, arrays=FAKE, ext=FAKE):
+    return ps.paged_desc(batch, lx, page, pages, arrays, arrays, arrays, mx, ext, ext)
+
+
+@pytest.mark.parametrize("desc_kw,kw,status", [
+    (dict(lx=0), {}, ps.E_INVAL),
+    (dict(page=0), {}, ps.E_INVAL),
+    (dict(mx=64 * 16 + 1), {}, ps.E_INVAL),
+    (dict(arrays=0), {}, ps.E_INVAL),
+    (dict(ext=0), {}, ps.E_INVAL),
+    (dict(lx=40), dict(hq=8, hkv=2), ps.E_UNSUPPORTED),   # 40 * 4 rows > 128
+    ({}, dict(ks=-1.0), ps.E_INVAL),
+    ({}, dict(vs=float("inf")), ps.E_INVAL),
+    ({}, {}, ps.E_WORKSPACE),                             # workspace missing
+    ({}, dict(ws=FAKE, wsb=16), ps.E_WORKSPACE),          # workspace too small
+])
+def test_paged_validation(lib, desc_kw, kw, status):
+    args = dict(hq=8, hkv=2, d=128, qdt=ps.BF16, kvdt=ps.FP8)
+    args.update(kw)
+    assert _call(_paged(**desc_kw), **args) == status
+
+
+def test_workspace_misaligned(lib):
+    desc = _paged()
+    need = ps.psattn_workspace_size(desc, 8, 2, 128, ps.BF16, ps.FP8)
+    assert need > 0
+    assert _call(desc, hq=8, hkv=2, d=128, qdt=ps.BF16, kvdt=ps.FP8, ws=FAKE + 16, wsb=need) == ps.E_INVAL
+
+
+def test_workspace_size_formula(lib):
+    desc = _paged(batch=3, lx=4, mx=1000)
+    info = ps.plan_info(desc, 8, 2, 128, ps.BF16, ps.BF16)
+    rows = 4 * 4
+    prow = 3 * 2 * info.n_splits * rows
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert ps.psattn_workspace_size(desc, 8, 2, 128, ps.BF16, ps.BF16) == r256(prow * 128 * 4) + r256(prow * 4)
+    assert ps.psattn_workspace_size(_flat(), 2, 2, 64, ps.F32, ps.F32) == 0
+    assert ps.psattn_workspace_size(None, 2, 2, 64, ps.F32, ps.F32) == 0
+
+
+# ---------------------------------------------------------------------------
+# planner (host copy of the device code) vs the oracle enumeration
+# ---------------------------------------------------------------------------
+def _plan_host(desc, hq, hkv, d, qdt, kvdt):
+    info = ps.PsattnPlanInfo()
+    ps.check(ps.psattn_plan_host(desc, hq, hkv, d, qdt, kvdt, 0, 0, info))
+    items = np.zeros((max(info.n_items, 1), ps.ITEM_FIELDS), dtype=np.int32)
+    ps.check(ps.psattn_plan_host(desc, hq, hkv, d, qdt, kvdt, items.ctypes.data, info.n_items, info))
+    return info, items[:info.n_items]
+
+
+def _flat_plan(p, lens, hq, hkv, d=128, dt=ps.BF16):
+    offs = np.concatenate([[p], p + np.cumsum(lens)]).astype(np.int32) if len(lens) else np.array([p], np.int32)
+    desc = ps.flat_desc(int(offs[-1]), p, len(lens), offs.ctypes.data if len(lens) else 0,
+                        max(lens) if len(lens) else 0)
+    info, items = _plan_host(desc, hq, hkv, d, dt, dt)
+    return offs, info, items
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_flat_planner_matches_enumeration(lib, case):
+    rng = np.random.default_rng(case)
+    p = int(rng.integers(0, 300))
+    n = int(rng.integers(0, 6))
+    lens = [int(x) for x in rng.integers(0, 200, size=n)]
+    if n == 0 and p == 0:
+        p = 5
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    offs, info, items = _flat_plan(p, lens, g * hkv, hkv, d=int(rng.choice([64, 128, 256])))
+    assert info.tile_tokens == 128 // g
+    ref = enumerate_flat(p, offs, hkv, info.tile_tokens)
+    assert np.array_equal(items, ref)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_flat_planner_items_cover_visible_pairs_once(lib, case):
+    rng = np.random.default_rng(100 + case)
+    p = int(rng.integers(0, 70))
+    lens = [int(x) for x in rng.integers(0, 60, size=int(rng.integers(1, 4)))]
+    hkv = 2
+    g = int(rng.choice([4, 8, 16, 32]))   # small tiles so that tiles are ragged
+    offs, info, items = _flat_plan(p, lens, g * hkv, hkv)
+    cnt = coverage_flat(items, p, offs, hkv)
+    t_n = int(offs[-1])
+    vis = np.array([[visible(r, c, p, offs) for c in range(t_n)] for r in range(t_n)], dtype=np.int64)
+    for h in range(hkv):
+        assert np.array_equal(cnt[h], vis)
+
+
+@pytest.mark.parametrize("name", ["tiny", "grpo", "grpo_ragged"])
+def test_flat_planner_on_named_workloads(lib, name):
+    inst = make_config(name)
+    offs = inst.seg_offsets
+    desc = ps.flat_desc(inst.total_tokens, inst.prefix_len, inst.num_segments, offs.ctypes.data,
+                        inst.max_seg_len)
+    info, items = _plan_host(desc, inst.hq, inst.hkv, inst.d, inst.dtype, inst.dtype)
+    assert np.array_equal(items, enumerate_flat(inst.prefix_len, offs, inst.hkv, info.tile_tokens))
+
+
+@pytest.mark.parametrize("prefix_lens,lx,hq,hkv,d,kvdt", [
+    ([16384] * 8, 4, 32, 8, 128, ps.BF16),
+    ([32768] * 4, 8, 16, 2, 256, ps.FP8),
+    ([100, 0, 5000, 17], 3, 8, 2, 64, ps.BF16),
+    ([0], 1, 4, 4, 128, ps.F32),
+    ([4096] * 2, 4, 16, 2, 256, ps.BF16),
+])
+def test_paged_planner_matches_enumeration(lib, prefix_lens, lx, hq, hkv, d, kvdt):
+    pl = np.asarray(prefix_lens, dtype=np.int32)
+    n_pages = int(sum((x + 15) // 16 for x in prefix_lens)) + 1
+    desc = ps.paged_desc(len(pl), lx, 16, n_pages, pl.ctypes.data, FAKE, FAKE, int(pl.max()), FAKE, FAKE)
+    qdt = ps.F32 if kvdt == ps.F32 else ps.BF16
+    info, items = _plan_host(desc, hq, hkv, d, qdt, kvdt)
+    assert info.split_len % 16 == 0 and info.split_len % info.kv_tile == 0
+    assert info.n_splits * info.split_len >= pl.max()
+    ref = enumerate_paged(pl, hkv, lx, info.n_splits, info.split_len)
+    assert np.array_equal(items, ref)
