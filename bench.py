@@ -90,6 +90,12 @@ class FlatRunner:
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
 
+    def grid_threads(self) -> int:
+        d = self.ps.flat_desc(self.inst.total_tokens, self.inst.prefix_len, self.inst.num_segments,
+                              self.seg.data_ptr(), self.inst.max_seg_len)
+        info = self.ps.plan_info(d, self.inst.hq, self.inst.hkv, self.inst.d, self.inst.dtype, self.inst.dtype)
+        return int(info.n_items) * 256
+
     def __call__(self):
         self.ps.fwd_flat(self.q, self.k, self.v, self.inst.prefix_len, self.seg, self.inst.max_seg_len,
                          sm_scale=self.inst.sm_scale, out=self.o, lse=self.lse)
@@ -193,21 +199,26 @@ def cpu_baseline(inst, flops_fn):
                       f"float64 build_kv expansion, {dt:.2f} s"}
 
 
-def traffic_from_profile(kernel: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def traffic_from_profile(kernel_prefix: str, grid: int):
+    """HBM bytes (read + written) per launch of a kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the factors that a
+    plain copy of known size gave in the same runs.  None when the counters
+    were taken on a different kernel source."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    path = os.path.join(ROOT, "profiles", "all_workloads_counters.json")
     src = os.path.join(ROOT, "prefix_shared_block_amd", "csrc", "psattn_kernels.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if prof.get("kernel_source_sha256") != h:
+    if prof.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
-    return prof.get("hbm_bytes_per_launch")
+    for key, v in prof.get("per_kernel", {}).items():
+        name, g = key.rsplit("|", 1)
+        if kernel_prefix in name and int(g) == grid:
+            return round(v["read_bytes"] + v["write_bytes"])
+    return None
 
 
 def main():
@@ -216,6 +227,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--all", action="store_true", help="also time the fp8 verify and ragged GRPO workloads")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (known bytes) to scale profiler byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     args = ap.parse_args()
@@ -244,7 +257,7 @@ def main():
     g_flops = flat_useful_flops(g_inst)
     g_tflops = g_flops / (tg["mean"] * 1e-3) / 1e12
     g_tflops_best = g_flops / (tg["min"] * 1e-3) / 1e12
-    traffic = traffic_from_profile("flat_fwd", "grpo")
+    traffic = traffic_from_profile("flat_fwd_kernel<128, false>", grpo.grid_threads())
     out = {
         "metric": METRIC,
         "value": round(g_tflops, 2),
@@ -307,6 +320,16 @@ def main():
         out["grpo_ragged"] = {"ms": round(tr["mean"], 4), "useful_tflops": round(rf / (tr["mean"] * 1e-3) / 1e12, 2),
                               "frac_mfma": round(rf / (tr["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del rr
+
+    if args.copy_calib:
+        n = (256 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calib_bytes"] = {"read": n * 4, "write": n * 4}
+        del src, dst
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu baseline)")
