@@ -12,8 +12,10 @@ bf16 ("verify us @16k", with its HBM GB/s against the algorithmic bytes that
 count every prefix K/V byte once), and, with --all, the fp8 verify and the
 large ragged GRPO workloads.
 
-Every timed call is preceded (outside the timed events) by a 1 GiB write that
-evicts L2 and the 256 MiB MALL, so every K/V byte is read from HBM.
+Every timed call is preceded (outside the timed events) by a 1 GiB read
+(a reduction over a scratch buffer) that evicts L2 and the 256 MiB MALL, so
+every K/V byte is read from HBM.  A read is used rather than a write so that
+no dirty lines are left to be written back while the timed kernel runs.
 Correctness against the float64 oracle is checked before timing.
 """
 from __future__ import annotations
@@ -158,20 +160,25 @@ class PagedRunner:
                        kind_of(i.q_dtype, i.kv_dtype), i.name)
 
 
+def evict(flush):
+    """Read 1 GiB so that L2 and the MALL hold none of the workload's bytes."""
+    return flush.sum()
+
+
 def time_calls(fn, flush, steps: int, warmup: int):
-    """Median-free plain timing: mean, min and p50 of per-call event times (ms),
-    each call preceded by a cache-evicting write outside the events."""
+    """Mean, min and p50 of per-call event times (ms), each call preceded by a
+    cache-evicting read outside the events."""
     import torch
 
     for _ in range(warmup):
-        flush.zero_()
+        evict(flush)
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        flush.zero_()
+        evict(flush)
         starts[i].record()
         fn()
         ends[i].record()
@@ -199,20 +206,32 @@ def cpu_baseline(inst, flops_fn):
                       f"float64 build_kv expansion, {dt:.2f} s"}
 
 
+def kernel_source_digest() -> str:
+    """sha256 over every kernel source file (csrc/*.hip, *.h, *.cpp, sorted by
+    name): profiler counters are only reused while this digest is unchanged."""
+    import hashlib
+
+    csrc = os.path.join(ROOT, "prefix_shared_block_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel_prefix: str, grid: int):
     """HBM bytes (read + written) per launch of a kernel, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the factors that a
     plain copy of known size gave in the same runs.  None when the counters
     were taken on a different kernel source."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", "all_workloads_counters.json")
-    src = os.path.join(ROOT, "prefix_shared_block_amd", "csrc", "psattn_kernels.hip")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    if prof.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if prof.get("kernel_source_sha256") != kernel_source_digest():
         return None
     for key, v in prof.get("per_kernel", {}).items():
         name, g = key.rsplit("|", 1)
@@ -243,7 +262,7 @@ def main():
 
     ps.load()
     torch.cuda.set_device(0)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     log("generating grpo workload")
     g_inst = make_config("grpo")

@@ -51,8 +51,14 @@ struct PagedArgs {
 
 // dtype codes follow psattn_dtype (0 f32, 1 bf16, 2 fp8 e4m3fn)
 int launch_flat(const FlatArgs& a, int d, int dtype, int64_t n_blocks, void* stream);
-int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, int row_blocks,
+struct PagedGeom;
+int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const PagedGeom& geo,
                  int64_t n_blocks, void* stream);
+// streaming prefix pass (bf16 / fp8 K/V), defined in psattn_stream.hip
+int launch_paged_stream(const PagedArgs& a, int d, int kv_dtype, const PagedGeom& geo, int64_t n_blocks,
+                        void* stream);
+// log-sum-exp combine + draft block, defined in psattn_kernels.hip
+int launch_paged_combine(const PagedArgs& a, int d, int q_dtype, int kv_dtype, void* stream);
 int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,
                      int32_t* items, void* stream);
 const char* hip_error_string(int err);

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #if defined(__HIPCC__)
+#include <hip/hip_runtime.h>
 #define PS_HD __host__ __device__ __forceinline__
 #else
 #define PS_HD inline
@@ -69,52 +70,136 @@ PS_HD FlatGeom flat_geom(int32_t g, int32_t d) {
   return f;
 }
 
-// Paged: R = draft_len * G rows, split into row blocks of 32; the 4 waves
-// are row_blocks x key_streams.  Each wave eats 32 keys per iteration, so
-// one iteration of the workgroup loads key_streams * 32 keys.
+// Paged.  R = draft_len * G stacked rows.  Two prefix-pass kernels:
+//  * streaming (bf16 / fp8 K/V, R <= 64, power-of-two pages): key stages are
+//    copied global -> LDS into a ring of slots, several stages ahead.
+//    - R <= 16 with bf16: one-wave workgroups over 16-key stages (3 slots),
+//      the wave holding all rows and head-dim columns, no barriers;
+//    - otherwise: four-wave workgroups over 32-key stages (ring as deep as
+//      128 KiB of LDS allows, at most 8 slots); the waves split the rows into
+//      row_groups groups of qblocks 16-row blocks and the head dimension into
+//      4 / row_groups slices;
+//  * tiled (otherwise): R in 32-row blocks over 4 waves (row_blocks x
+//    key_streams), key tiles of key_streams * 32 keys shared through LDS.
 struct PagedGeom {
   int32_t rows;         // draft_len * G
-  int32_t row_blocks;   // ceil(rows / 32) in {1, 2, 4}
-  int32_t key_streams;  // 4 / row_blocks
-  int32_t kv_tile;      // keys per workgroup iteration = key_streams * 32
+  int32_t stream;       // 1: streaming kernel, 0: tiled kernel
+  int32_t waves;        // waves per workgroup
+  int32_t stage_keys;   // streaming: keys per stage (16 or 32)
+  int32_t ring;         // streaming: LDS slots
+  int32_t max_pages;    // streaming: page-table entries kept in LDS
+  int32_t qblocks;      // streaming: 16-row blocks per wave
+  int32_t row_groups;   // streaming: row groups (head-dim slices = waves / row_groups)
+  int32_t row_blocks;   // tiled: 32-row blocks (1, 2 or 4)
+  int32_t key_streams;  // tiled: 4 / row_blocks
+  int32_t kv_tile;      // keys consumed by one workgroup iteration
+  int32_t wg_per_cu;    // workgroups one CU can hold (LDS-limited estimate)
 };
 
-PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, bool f32) {
+constexpr int32_t kStreamMaxPages = 512;       // four-wave workgroups
+constexpr int32_t kStreamMaxPagesSmall = 128;  // one-wave workgroups
+constexpr int32_t kLdsPerCu = 160 * 1024;
+
+PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, int32_t kv_dtype,
+                           int32_t page_size) {
   PagedGeom p;
   p.rows = draft_len * g;
+  const int32_t es = kv_dtype == 0 ? 4 : (kv_dtype == 1 ? 2 : 1);
+  const bool pow2_pages = page_size > 0 && (page_size & (page_size - 1)) == 0;
+  p.stream = (kv_dtype != 0 && p.rows <= 64 && pow2_pages) ? 1 : 0;
+  p.row_blocks = 0;
+  p.key_streams = 0;
+  if (p.stream) {
+    int32_t lds;
+    if (kv_dtype == 1 && p.rows <= 16) {
+      p.waves = 1;
+      p.stage_keys = 16;
+      p.ring = 3;
+      p.max_pages = kStreamMaxPagesSmall;
+      p.qblocks = 1;
+      p.row_groups = 1;
+      lds = p.ring * 2 * p.stage_keys * d * es + 4 * p.max_pages;
+      p.wg_per_cu = kLdsPerCu / lds;
+      if (p.wg_per_cu > 8) p.wg_per_cu = 8;
+    } else {
+      p.waves = kWaves;
+      p.stage_keys = 32;
+      const int32_t slot = 2 * p.stage_keys * d * es;
+      p.ring = 131072 / slot > 8 ? 8 : 131072 / slot;
+      p.max_pages = kStreamMaxPages;
+      if (p.rows <= 16) {
+        p.qblocks = 1;
+        p.row_groups = 1;
+      } else if (p.rows <= 32) {
+        p.qblocks = 1;
+        p.row_groups = 2;
+      } else if (d >= 256) {  // keep 256-wide rows at one block per wave (register budget)
+        p.qblocks = 1;
+        p.row_groups = 4;
+      } else {
+        p.qblocks = 2;
+        p.row_groups = 2;
+      }
+      lds = p.ring * slot + 4 * p.max_pages;
+      p.wg_per_cu = kLdsPerCu / lds;
+    }
+    p.kv_tile = p.stage_keys;
+    return p;
+  }
   int32_t rb = cdiv32(p.rows, kWaveRows);
+  p.waves = kWaves;
+  p.stage_keys = 0;
+  p.ring = 0;
+  p.max_pages = 0;
+  p.qblocks = 0;
+  p.row_groups = 0;
   p.row_blocks = rb <= 1 ? 1 : (rb <= 2 ? 2 : 4);
   // fp32 K and V tiles of 128 keys x 256 would not fit in LDS: use 64 keys
-  if (f32 && d >= 256 && p.row_blocks == 1) p.row_blocks = 2;
+  if (kv_dtype == 0 && d >= 256 && p.row_blocks == 1) p.row_blocks = 2;
   p.key_streams = kWaves / p.row_blocks;
   p.kv_tile = p.key_streams * kWaveRows;
+  p.wg_per_cu = 2;
   return p;
 }
 
-// Split heuristic: aim at about 512 workgroups (two per CU on a 256-CU part)
-// without making a split shorter than one workgroup iteration.  Depends only
-// on shapes, so the workspace size is a pure function of the descriptor.
-constexpr int32_t kTargetWorkgroups = 512;
-
+// Split heuristic: aim at filling every CU of a 256-CU part with as many
+// workgroups as its LDS holds, without making a split shorter than one
+// workgroup iteration, without letting the fp32 partial results (R x D x 4
+// bytes per split) exceed an eighth of the K/V bytes a split reads, and (for
+// the streaming kernel) with the split's page list fitting in LDS.  Depends
+// only on shapes, so the workspace size is a pure function of the descriptor.
 struct Splits {
   int32_t n_splits;
   int32_t split_len;
 };
 
-PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, int32_t kv_tile) {
+PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, int32_t page_size,
+                          int32_t d, int32_t kv_dtype, const PagedGeom& geo) {
   Splits s;
+  const int32_t kv_tile = geo.kv_tile;
   int64_t pairs = (int64_t)batch * hkv;
   if (pairs <= 0 || max_prefix_len <= 0) {
     s.n_splits = 1;
     s.split_len = kv_tile;
     return s;
   }
-  int64_t want = cdiv64(kTargetWorkgroups, pairs);
+  const int64_t es = kv_dtype == 0 ? 4 : (kv_dtype == 1 ? 2 : 1);
+  const int64_t target = 256 * (int64_t)(geo.wg_per_cu > 0 ? geo.wg_per_cu : 1);
+  int64_t want = cdiv64(target, pairs);
+  // partial bytes per split <= K/V bytes per split / 8
+  const int64_t min_len = cdiv64(16 * (int64_t)geo.rows, es);
+  const int64_t max_by_partials = max_prefix_len / (min_len > 0 ? min_len : 1);
+  if (want > max_by_partials) want = max_by_partials;
   int64_t max_n = cdiv64(max_prefix_len, kv_tile);
   int64_t n = want < max_n ? want : max_n;
   if (n < 1) n = 1;
   int64_t per = cdiv64(max_prefix_len, n);
   int64_t len = cdiv64(per, kv_tile) * kv_tile;
+  if (geo.stream) {
+    int64_t cap = ((int64_t)(geo.max_pages - 2) * page_size / kv_tile) * kv_tile;
+    if (cap < kv_tile) cap = kv_tile;
+    if (len > cap) len = cap;
+  }
   s.split_len = (int32_t)len;
   s.n_splits = (int32_t)cdiv64(max_prefix_len, len);
   return s;

@@ -106,8 +106,8 @@ psattn_status check_common(const psattn_desc* d, int32_t hq, int32_t hkv, int32_
       return fail(PSATTN_E_UNSUPPORTED, "draft_len * G = %lld exceeds %d stacked rows", (long long)rows,
                   kWaves * kWaveRows);
     if ((int64_t)d->batch * d->draft_len > INT32_MAX / 2) return fail(PSATTN_E_UNSUPPORTED, "batch too large");
-    plan->pg = paged_geom(d->draft_len, plan->g, hd, kv_dt == PSATTN_F32);
-    plan->sp = paged_splits(d->batch, hkv, d->max_prefix_len, plan->pg.kv_tile);
+    plan->pg = paged_geom(d->draft_len, plan->g, hd, (int32_t)kv_dt, d->page_size);
+    plan->sp = paged_splits(d->batch, hkv, d->max_prefix_len, d->page_size, hd, (int32_t)kv_dt, plan->pg);
     plan->paged_blocks = (int64_t)d->batch * hkv * plan->sp.n_splits;
     if (plan->paged_blocks > INT32_MAX) return fail(PSATTN_E_UNSUPPORTED, "grid too large");
     const size_t prow = (size_t)d->batch * hkv * plan->sp.n_splits * plan->pg.rows;
@@ -229,7 +229,7 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
     a.split_len = p.sp.split_len;
     a.scale_log2 = sm_scale * k_scale * log2e;
     a.v_scale = v_scale;
-    err = launch_paged(a, d, (int)q_dtype, (int)kv_dtype, p.pg.row_blocks, p.paged_blocks, stream);
+    err = launch_paged(a, d, (int)q_dtype, (int)kv_dtype, p.pg, p.paged_blocks, stream);
   }
   if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
   return PSATTN_OK;

@@ -26,78 +26,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_common.h"
 #include "launch.h"
 #include "plan.h"
 
 namespace psattn {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// finite stand-in for -inf as the initial running maximum, so that a row whose
-// first tile is fully masked gives exp2(-inf - (-1e30)) = 0, never NaN
-constexpr float kNegBig = -1.0e30f;
-
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
-
-template <int DT>
-struct Elem;
-template <>
-struct Elem<DT_F32> {
-  static constexpr int size = 4;
-};
-template <>
-struct Elem<DT_BF16> {
-  static constexpr int size = 2;
-};
-template <>
-struct Elem<DT_FP8> {
-  static constexpr int size = 1;
-};
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
-
-// value of the lane l ^ 32 (the other half of the wave, same query column)
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2_t v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// two OCP e4m3fn codes (the low or high 16 bits of w) -> two bf16 (exact)
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// 16 fp8 codes -> 16 bf16 (two 16-byte chunks)
-__device__ __forceinline__ void fp8x16_to_bf16(const u32x4_t in, u32x4_t& lo, u32x4_t& hi) {
-  lo[0] = fp8x2_to_bf16x2<false>(in[0]);
-  lo[1] = fp8x2_to_bf16x2<true>(in[0]);
-  lo[2] = fp8x2_to_bf16x2<false>(in[1]);
-  lo[3] = fp8x2_to_bf16x2<true>(in[1]);
-  hi[0] = fp8x2_to_bf16x2<false>(in[2]);
-  hi[1] = fp8x2_to_bf16x2<true>(in[2]);
-  hi[2] = fp8x2_to_bf16x2<false>(in[3]);
-  hi[3] = fp8x2_to_bf16x2<true>(in[3]);
-}
-
-__device__ __forceinline__ uint32_t half_of(const u32x4_t& x, int e) {
-  // 16-bit element e (0..7) of an 8 x 16-bit chunk
-  return (x[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
-}
 
 // ---------------------------------------------------------------------------
 // LDS tile geometry.  bf16 compute: K row-major [BN][D+8], V transposed
@@ -660,38 +593,18 @@ void paged_split_kernel(PagedArgs a) {
 // Combine: merge splits by log-sum-exp and fold in the causal draft block.
 // One wave per (request, kv head, stacked row).
 // ===========================================================================
-template <int DT>
-__device__ __forceinline__ float load_elem(const void* base, size_t idx) {
-  if constexpr (DT == DT_F32) {
-    return reinterpret_cast<const float*>(base)[idx];
-  } else if constexpr (DT == DT_BF16) {
-    uint32_t u = reinterpret_cast<const uint16_t*>(base)[idx];
-    return __builtin_bit_cast(float, u << 16);
-  } else {
-    uint32_t u = reinterpret_cast<const uint8_t*>(base)[idx];
-    uint32_t w = fp8x2_to_bf16x2<false>(u) & 0xFFFFu;
-    return __builtin_bit_cast(float, w << 16);
-  }
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
+// One wave per (request, kv head, stacked row, 64-column chunk of the head
+// dimension): the draft-block logits need the full head dimension (each wave
+// recomputes them; they are tiny), the merge touches only the wave's chunk.
 template <int D, int QDT, int KDT>
 __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float scale_log2_draft) {
-  constexpr int PER = D / 64;  // d elements per lane: d = lane + 64 * e
-  const int wave = (blockIdx.x * 256 + threadIdx.x) >> 6;
+  constexpr int PER = D / 64;  // d elements per lane for the dot products: d = lane + 64 * e
+  const int gw = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
-  const int total = a.batch * a.hkv * a.rows;
-  if (wave >= total) return;
+  const int total = a.batch * a.hkv * a.rows * PER;
+  if (gw >= total) return;
+  const int chunk = gw % PER;
+  const int wave = gw / PER;
   const int r = wave % a.rows;
   const int h_kv = (wave / a.rows) % a.hkv;
   const int b = wave / (a.rows * a.hkv);
@@ -699,23 +612,21 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
   const int hl = r - t * a.g;
   const int head = h_kv * a.g + hl;
   const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + head;
+  const int dcol = chunk * 64 + lane;
 
-  // prefix splits
+  // max over the splits' log-sum-exps (log2 domain)
   const size_t prow0 = (((size_t)b * a.hkv + h_kv) * a.n_splits) * a.rows + r;
   float mp = -__builtin_inff();
   for (int s = lane; s < a.n_splits; s += 64) mp = fmaxf(mp, a.part_lse[prow0 + (size_t)s * a.rows]);
   mp = wave_max(mp);
 
-  // draft block: keys 0..t of this request's draft K/V (causal)
+  // draft block: keys 0..t of this request's draft K/V (causal), online softmax
   float q[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) q[e] = load_elem<QDT>(a.q, qrow * D + lane + 64 * e);
-  // online softmax over the draft keys j = 0..t
   float md = -__builtin_inff();
   float ld = 0.f;
-  float od[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) od[e] = 0.f;
+  float od = 0.f;
   for (int j = 0; j <= t; ++j) {
     const size_t krow = ((size_t)(b * a.draft_len + j) * a.hkv + h_kv) * D;
     float zz = 0.f;
@@ -726,39 +637,43 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
     const float a1 = fast_exp2(md - mn);
     const float p = fast_exp2(zz - mn);
     ld = ld * a1 + p;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) od[e] = od[e] * a1 + p * load_elem<KDT>(a.v_ext, krow + lane + 64 * e);
+    od = od * a1 + p * load_elem<KDT>(a.v_ext, krow + dcol);
     md = mn;
   }
   const float lse_d = md + fast_log2(ld);
 
+  // merge: weights exp2(LSE_s - M); an empty split has LSE_s = -inf, O_s = 0
   const float mt = fmaxf(mp, lse_d);
   const float wd = fast_exp2(lse_d - mt);
   float wsum = wd;
-  float acc[PER];
+  float acc = od * (wd / ld);
+  const float* po = a.part_o + prow0 * D + dcol;
+  const size_t sstride = (size_t)a.rows * D;
+  int s = 0;
+  for (; s + 8 <= a.n_splits; s += 8) {
+    float w[8], x[8];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = od[e] * (wd / ld);
-  for (int s = 0; s < a.n_splits; ++s) {
-    const size_t prow = prow0 + (size_t)s * a.rows;
-    const float ls = a.part_lse[prow];
-    const float w = fast_exp2(ls - mt);  // 0 for an empty split (ls = -inf)
-    if (w > 0.f) {
-      wsum += w;
-      const float* po = a.part_o + prow * D;
+    for (int u = 0; u < 8; ++u) {
+      w[u] = fast_exp2(a.part_lse[prow0 + (size_t)(s + u) * a.rows] - mt);
+      x[u] = po[(size_t)(s + u) * sstride];
+    }
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += w * po[lane + 64 * e];
+    for (int u = 0; u < 8; ++u) {
+      wsum += w[u];
+      acc += w[u] * x[u];
     }
   }
-  const float sc = a.v_scale / wsum;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float v = acc[e] * sc;
-    if constexpr (QDT == DT_F32)
-      reinterpret_cast<float*>(a.o)[qrow * D + lane + 64 * e] = v;
-    else
-      reinterpret_cast<__bf16*>(a.o)[qrow * D + lane + 64 * e] = (__bf16)v;
+  for (; s < a.n_splits; ++s) {
+    const float w = fast_exp2(a.part_lse[prow0 + (size_t)s * a.rows] - mt);
+    wsum += w;
+    acc += w * po[(size_t)s * sstride];
   }
-  if (lane == 0) a.lse[qrow] = (mt + fast_log2(wsum)) * kLn2;
+  const float v = acc * (a.v_scale / wsum);
+  if constexpr (QDT == DT_F32)
+    reinterpret_cast<float*>(a.o)[qrow * D + dcol] = v;
+  else
+    reinterpret_cast<__bf16*>(a.o)[qrow * D + dcol] = (__bf16)v;
+  if (lane == 0 && chunk == 0) a.lse[qrow] = (mt + fast_log2(wsum)) * kLn2;
 }
 
 // ===========================================================================
@@ -827,43 +742,54 @@ static int launch_split_rb(const PagedArgs& a, int rb, int64_t n_blocks, hipStre
 }
 
 template <int D, int QDT, int KDT>
-static int launch_combine_t(const PagedArgs& a, hipStream_t s, float sld) {
-  const int64_t waves = (int64_t)a.batch * a.hkv * a.rows;
+static int launch_combine_t(const PagedArgs& a, hipStream_t s) {
+  const int64_t waves = (int64_t)a.batch * a.hkv * a.rows * (D / 64);
   const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((paged_combine_kernel<D, QDT, KDT>), dim3((unsigned)blocks), dim3(256), 0, s, a, sld);
+  hipLaunchKernelGGL((paged_combine_kernel<D, QDT, KDT>), dim3((unsigned)blocks), dim3(256), 0, s, a, a.scale_log2);
   return (int)hipGetLastError();
 }
 
 template <int D>
-static int launch_paged_d(const PagedArgs& a, int q_dtype, int kv_dtype, int rb, int64_t n_blocks,
-                          hipStream_t s) {
-  int e;
-  const float sld = a.scale_log2;
-  if (kv_dtype == DT_F32) {
-    e = launch_split_rb<D, DT_F32>(a, rb, n_blocks, s);
-    if (e) return e;
-    return launch_combine_t<D, DT_F32, DT_F32>(a, s, sld);
-  }
-  if (kv_dtype == DT_BF16) {
-    e = launch_split_rb<D, DT_BF16>(a, rb, n_blocks, s);
-    if (e) return e;
-    return launch_combine_t<D, DT_BF16, DT_BF16>(a, s, sld);
-  }
-  e = launch_split_rb<D, DT_FP8>(a, rb, n_blocks, s);
-  if (e) return e;
-  (void)q_dtype;
-  return launch_combine_t<D, DT_BF16, DT_FP8>(a, s, sld);
+static int launch_combine_d(const PagedArgs& a, int kv_dtype, hipStream_t s) {
+  if (kv_dtype == DT_F32) return launch_combine_t<D, DT_F32, DT_F32>(a, s);
+  if (kv_dtype == DT_BF16) return launch_combine_t<D, DT_BF16, DT_BF16>(a, s);
+  return launch_combine_t<D, DT_BF16, DT_FP8>(a, s);
 }
 
-int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, int row_blocks,
-                 int64_t n_blocks, void* stream) {
+int launch_paged_combine(const PagedArgs& a, int d, int q_dtype, int kv_dtype, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)q_dtype;  // q dtype follows kv dtype: f32 with f32, bf16 otherwise
   switch (d) {
-    case 64: return launch_paged_d<64>(a, q_dtype, kv_dtype, row_blocks, n_blocks, s);
-    case 128: return launch_paged_d<128>(a, q_dtype, kv_dtype, row_blocks, n_blocks, s);
-    case 256: return launch_paged_d<256>(a, q_dtype, kv_dtype, row_blocks, n_blocks, s);
+    case 64: return launch_combine_d<64>(a, kv_dtype, s);
+    case 128: return launch_combine_d<128>(a, kv_dtype, s);
+    case 256: return launch_combine_d<256>(a, kv_dtype, s);
   }
   return (int)hipErrorInvalidValue;
+}
+
+template <int D>
+static int launch_tiled_d(const PagedArgs& a, int kv_dtype, int rb, int64_t n_blocks, hipStream_t s) {
+  if (kv_dtype == DT_F32) return launch_split_rb<D, DT_F32>(a, rb, n_blocks, s);
+  if (kv_dtype == DT_BF16) return launch_split_rb<D, DT_BF16>(a, rb, n_blocks, s);
+  return launch_split_rb<D, DT_FP8>(a, rb, n_blocks, s);
+}
+
+int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const PagedGeom& geo,
+                 int64_t n_blocks, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int e;
+  if (geo.stream) {
+    e = launch_paged_stream(a, d, kv_dtype, geo, n_blocks, stream);
+  } else {
+    switch (d) {
+      case 64: e = launch_tiled_d<64>(a, kv_dtype, geo.row_blocks, n_blocks, s); break;
+      case 128: e = launch_tiled_d<128>(a, kv_dtype, geo.row_blocks, n_blocks, s); break;
+      case 256: e = launch_tiled_d<256>(a, kv_dtype, geo.row_blocks, n_blocks, s); break;
+      default: e = (int)hipErrorInvalidValue;
+    }
+  }
+  if (e) return e;
+  return launch_paged_combine(a, d, q_dtype, kv_dtype, stream);
 }
 
 int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,
