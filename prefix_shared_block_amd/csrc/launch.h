@@ -57,6 +57,11 @@ int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const Pag
 // streaming prefix pass (bf16 / fp8 K/V), defined in psattn_stream.hip
 int launch_paged_stream(const PagedArgs& a, int d, int kv_dtype, const PagedGeom& geo, int64_t n_blocks,
                         void* stream);
+// register-streamed prefix pass with the draft block folded into each
+// request's last split (bf16 / fp8 K/V, R <= 16), and the matching merge of
+// the splits (no draft work), defined in psattn_regstream.hip
+int launch_paged_reg(const PagedArgs& a, int d, int kv_dtype, int64_t n_blocks, void* stream);
+int launch_paged_merge(const PagedArgs& a, int d, int q_dtype, void* stream);
 // log-sum-exp combine + draft block, defined in psattn_kernels.hip
 int launch_paged_combine(const PagedArgs& a, int d, int q_dtype, int kv_dtype, void* stream);
 int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,

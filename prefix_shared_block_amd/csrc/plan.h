@@ -70,8 +70,13 @@ PS_HD FlatGeom flat_geom(int32_t g, int32_t d) {
   return f;
 }
 
-// Paged.  R = draft_len * G stacked rows.  Two prefix-pass kernels:
-//  * streaming (bf16 / fp8 K/V, R <= 64, power-of-two pages): key stages are
+// Paged.  R = draft_len * G stacked rows.  Three prefix-pass kernels:
+//  * register streaming (stream == 2: bf16 / fp8 K/V, R <= 16, power-of-two
+//    pages of >= 16 slots): reg_waves(d) waves per workgroup, each streaming
+//    its own run of 16-key stages straight into registers several stages
+//    ahead (no LDS page table, no barriers), merged in LDS at the end;
+//  * LDS streaming (stream == 1: bf16 / fp8 K/V, R <= 64, power-of-two
+//    pages): key stages are
 //    copied global -> LDS into a ring of slots, several stages ahead.
 //    - R <= 16 with bf16: one-wave workgroups over 16-key stages (3 slots),
 //      the wave holding all rows and head-dim columns, no barriers;
@@ -83,7 +88,7 @@ PS_HD FlatGeom flat_geom(int32_t g, int32_t d) {
 //    key_streams), key tiles of key_streams * 32 keys shared through LDS.
 struct PagedGeom {
   int32_t rows;         // draft_len * G
-  int32_t stream;       // 1: streaming kernel, 0: tiled kernel
+  int32_t stream;       // 2: register streaming, 1: LDS streaming, 0: tiled kernel
   int32_t waves;        // waves per workgroup
   int32_t stage_keys;   // streaming: keys per stage (16 or 32)
   int32_t ring;         // streaming: LDS slots
@@ -95,6 +100,10 @@ struct PagedGeom {
   int32_t kv_tile;      // keys consumed by one workgroup iteration
   int32_t wg_per_cu;    // workgroups one CU can hold (LDS-limited estimate)
 };
+
+// waves per workgroup of the register-streaming kernel (each wave streams
+// its own share of the split; 8 share a CU at two per SIMD up to D = 128)
+PS_HD constexpr int32_t reg_waves(int32_t d) { return d <= 128 ? 8 : 4; }
 
 constexpr int32_t kStreamMaxPages = 512;       // four-wave workgroups
 constexpr int32_t kStreamMaxPagesSmall = 128;  // one-wave workgroups
@@ -109,6 +118,19 @@ PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, int32_t kv_d
   p.stream = (kv_dtype != 0 && p.rows <= 64 && pow2_pages) ? 1 : 0;
   p.row_blocks = 0;
   p.key_streams = 0;
+  if (p.stream && p.rows <= 16 && page_size >= 16) {
+    p.stream = 2;
+    p.waves = reg_waves(d);
+    p.stage_keys = 16;
+    p.ring = 0;
+    p.max_pages = 0;
+    p.qblocks = 1;
+    p.row_groups = 1;
+    p.kv_tile = 16;
+    // register-limited residency: 8 waves per CU (16 for D = 64)
+    p.wg_per_cu = d <= 64 ? 2 : 1;
+    return p;
+  }
   if (p.stream) {
     int32_t lds;
     if (kv_dtype == 1 && p.rows <= 16) {
@@ -165,8 +187,9 @@ PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, int32_t kv_d
 // Split heuristic: aim at filling every CU of a 256-CU part with as many
 // workgroups as its LDS holds, without making a split shorter than one
 // workgroup iteration, without letting the fp32 partial results (R x D x 4
-// bytes per split) exceed an eighth of the K/V bytes a split reads, and (for
-// the streaming kernel) with the split's page list fitting in LDS.  Depends
+// bytes per split) exceed an eighth of the K/V bytes a split reads, with the
+// split's page list fitting in LDS (LDS streaming kernel) and with at most 64
+// splits (register streaming kernel).  Depends
 // only on shapes, so the workspace size is a pure function of the descriptor.
 struct Splits {
   int32_t n_splits;
@@ -190,12 +213,14 @@ PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, in
   const int64_t min_len = cdiv64(16 * (int64_t)geo.rows, es);
   const int64_t max_by_partials = max_prefix_len / (min_len > 0 ? min_len : 1);
   if (want > max_by_partials) want = max_by_partials;
+  // the register-streaming merge holds one split weight per lane
+  if (geo.stream == 2 && want > 64) want = 64;
   int64_t max_n = cdiv64(max_prefix_len, kv_tile);
   int64_t n = want < max_n ? want : max_n;
   if (n < 1) n = 1;
   int64_t per = cdiv64(max_prefix_len, n);
   int64_t len = cdiv64(per, kv_tile) * kv_tile;
-  if (geo.stream) {
+  if (geo.stream == 1) {
     int64_t cap = ((int64_t)(geo.max_pages - 2) * page_size / kv_tile) * kv_tile;
     if (cap < kv_tile) cap = kv_tile;
     if (len > cap) len = cap;

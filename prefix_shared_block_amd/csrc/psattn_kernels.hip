@@ -778,7 +778,11 @@ int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const Pag
                  int64_t n_blocks, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int e;
-  if (geo.stream) {
+  if (geo.stream == 2) {
+    e = launch_paged_reg(a, d, kv_dtype, n_blocks, stream);
+    if (e) return e;
+    return launch_paged_merge(a, d, q_dtype, stream);
+  } else if (geo.stream == 1) {
     e = launch_paged_stream(a, d, kv_dtype, geo, n_blocks, stream);
   } else {
     switch (d) {

@@ -150,6 +150,10 @@ def test_verify_gqa_ratios(gpu_lib, hq, hkv):
     ([777], 16, 8, 1, 128, FP8),                      # 128 stacked rows
     ([257, 1024], 4, 4, 2, 128, F32),                 # fp32
     ([2000], 2, 2, 1, 256, F32),                      # fp32, D = 256
+    ([3000, 1500, 0], 2, 8, 2, 128, FP8),             # fp8, 8 stacked rows, empty prefix
+    ([900, 2049], 16, 4, 4, 64, FP8),                 # fp8, D = 64, 16-token draft, G = 1
+    ([4100], 4, 8, 2, 256, FP8),                      # fp8, D = 256, 16 stacked rows
+    ([333, 16, 15], 16, 2, 2, 128, BF16),             # 16-token draft, one full / partial page
 ])
 def test_verify_edge_cases(gpu_lib, prefix_lens, lx, hq, hkv, d, kvdt):
     n_pages = int(sum((x + 15) // 16 for x in prefix_lens)) + 7
