@@ -62,6 +62,9 @@ int launch_paged_stream(const PagedArgs& a, int d, int kv_dtype, const PagedGeom
 // the splits (no draft work), defined in psattn_regstream.hip
 int launch_paged_reg(const PagedArgs& a, int d, int kv_dtype, int64_t n_blocks, void* stream);
 int launch_paged_merge(const PagedArgs& a, int d, int q_dtype, void* stream);
+// wide prefix pass (bf16 / fp8 K/V, 16 < R <= 64) with the draft block folded
+// into each request's last split, defined in psattn_widestream.hip
+int launch_paged_wide(const PagedArgs& a, int d, int kv_dtype, int64_t n_blocks, void* stream);
 // log-sum-exp combine + draft block, defined in psattn_kernels.hip
 int launch_paged_combine(const PagedArgs& a, int d, int q_dtype, int kv_dtype, void* stream);
 int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,

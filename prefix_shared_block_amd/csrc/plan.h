@@ -75,8 +75,12 @@ PS_HD FlatGeom flat_geom(int32_t g, int32_t d) {
 //    pages of >= 16 slots): reg_waves(d) waves per workgroup, each streaming
 //    its own run of 16-key stages straight into registers several stages
 //    ahead (no LDS page table, no barriers), merged in LDS at the end;
+//  * wide streaming (stream == 3: bf16 / fp8 K/V, 16 < R <= 64, power-of-two
+//    pages of >= 16 slots): four waves per workgroup share 64-key
+//    superstages converted to bf16 in LDS, each wave a 32-row x 32-key block
+//    of every superstage on 32x32 MFMAs;
 //  * LDS streaming (stream == 1: bf16 / fp8 K/V, R <= 64, power-of-two
-//    pages): key stages are
+//    pages of fewer than 16 slots): key stages are
 //    copied global -> LDS into a ring of slots, several stages ahead.
 //    - R <= 16 with bf16: one-wave workgroups over 16-key stages (3 slots),
 //      the wave holding all rows and head-dim columns, no barriers;
@@ -88,7 +92,7 @@ PS_HD FlatGeom flat_geom(int32_t g, int32_t d) {
 //    key_streams), key tiles of key_streams * 32 keys shared through LDS.
 struct PagedGeom {
   int32_t rows;         // draft_len * G
-  int32_t stream;       // 2: register streaming, 1: LDS streaming, 0: tiled kernel
+  int32_t stream;       // 3: wide, 2: register, 1: LDS streaming; 0: tiled kernel
   int32_t waves;        // waves per workgroup
   int32_t stage_keys;   // streaming: keys per stage (16 or 32)
   int32_t ring;         // streaming: LDS slots
@@ -118,6 +122,18 @@ PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, int32_t kv_d
   p.stream = (kv_dtype != 0 && p.rows <= 64 && pow2_pages) ? 1 : 0;
   p.row_blocks = 0;
   p.key_streams = 0;
+  if (p.stream && p.rows > 16 && page_size >= 16) {
+    p.stream = 3;
+    p.waves = kWaves;
+    p.stage_keys = 64;
+    p.ring = 0;
+    p.max_pages = 0;
+    p.qblocks = 0;
+    p.row_groups = 2;
+    p.kv_tile = 64;
+    p.wg_per_cu = 1;
+    return p;
+  }
   if (p.stream && p.rows <= 16 && page_size >= 16) {
     p.stream = 2;
     p.waves = reg_waves(d);
@@ -189,7 +205,7 @@ PS_HD PagedGeom paged_geom(int32_t draft_len, int32_t g, int32_t d, int32_t kv_d
 // workgroup iteration, without letting the fp32 partial results (R x D x 4
 // bytes per split) exceed an eighth of the K/V bytes a split reads, with the
 // split's page list fitting in LDS (LDS streaming kernel) and with at most 64
-// splits (register streaming kernel).  Depends
+// splits (register and wide streaming kernels).  Depends
 // only on shapes, so the workspace size is a pure function of the descriptor.
 struct Splits {
   int32_t n_splits;
@@ -213,8 +229,9 @@ PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, in
   const int64_t min_len = cdiv64(16 * (int64_t)geo.rows, es);
   const int64_t max_by_partials = max_prefix_len / (min_len > 0 ? min_len : 1);
   if (want > max_by_partials) want = max_by_partials;
-  // the register-streaming merge holds one split weight per lane
-  if (geo.stream == 2 && want > 64) want = 64;
+  // the merge of the register and wide streaming kernels holds one split
+  // weight per lane
+  if (geo.stream >= 2 && want > 64) want = 64;
   int64_t max_n = cdiv64(max_prefix_len, kv_tile);
   int64_t n = want < max_n ? want : max_n;
   if (n < 1) n = 1;

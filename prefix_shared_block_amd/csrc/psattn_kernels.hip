@@ -778,8 +778,9 @@ int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const Pag
                  int64_t n_blocks, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int e;
-  if (geo.stream == 2) {
-    e = launch_paged_reg(a, d, kv_dtype, n_blocks, stream);
+  if (geo.stream == 2 || geo.stream == 3) {
+    e = geo.stream == 2 ? launch_paged_reg(a, d, kv_dtype, n_blocks, stream)
+                        : launch_paged_wide(a, d, kv_dtype, n_blocks, stream);
     if (e) return e;
     return launch_paged_merge(a, d, q_dtype, stream);
   } else if (geo.stream == 1) {

@@ -14,8 +14,8 @@
 //    several of them.  The last split of each (request, kv head) also runs
 //    the causal draft block as one extra 16-key stage (draft row j sees draft
 //    keys 0..j), so its partial already contains it;
-//  * paged_merge_kernel: one wave per stacked row merges the splits' partial
-//    results by log-sum-exp and applies v_scale.
+//  * paged_merge_kernel: one wave per (stacked row, 64 columns) merges the
+//    splits' partial results by log-sum-exp and applies v_scale.
 //
 //  * keys are walked in 16-key stages.  A stage is one aligned 16-slot block
 //    of one page, so its page id and base address are wave-uniform (scalar
@@ -359,37 +359,39 @@ void paged_reg_kernel(PagedArgs a) {
   }
 }
 
-// Merge of the splits' partial results for one stacked row per wave:
-// O = v_scale * sum_s w_s O_s / sum_s w_s, LSE = ln 2 * (M + log2 sum_s w_s)
-// with w_s = exp2(LSE_s - M), M = max_s LSE_s (empty splits have LSE_s = -inf
-// and weight 0).  Lane l holds columns PER l .. PER l + PER - 1.  The first
-// MB splits' partials are loaded together with the log-sum-exps, so that a
-// row costs one memory round trip when n_splits <= MB.
+// Merge of the splits' partial results, one wave per (stacked row, 64-column
+// slice): O = v_scale * sum_s w_s O_s / sum_s w_s, LSE = ln 2 * (M + log2
+// sum_s w_s) with w_s = exp2(LSE_s - M), M = max_s LSE_s (empty splits have
+// LSE_s = -inf and weight 0).  Lane l holds one column; the partials of up to
+// MB splits are loaded together with the log-sum-exps, so that a wave costs
+// one memory round trip when n_splits <= MB.
 template <int D, int QDT>
 __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
-  constexpr int PER = D / 64;
-  constexpr int MB = 8;
-  typedef float fv_t __attribute__((ext_vector_type(PER)));
+  constexpr int NCH = D / 64;
+  constexpr int MB = 32;
   const int gw = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
-  if (gw >= a.batch * a.hkv * a.rows) return;
-  const int r = gw % a.rows;
-  const int h_kv = (gw / a.rows) % a.hkv;
-  const int b = gw / (a.rows * a.hkv);
+  if (gw >= a.batch * a.hkv * a.rows * NCH) return;
+  const int ch = gw % NCH;
+  const int rw = gw / NCH;
+  const int r = rw % a.rows;
+  const int h_kv = (rw / a.rows) % a.hkv;
+  const int b = rw / (a.rows * a.hkv);
   const int t = r / a.g;
   const int hl = r - t * a.g;
   const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
   const size_t prow0 = (((size_t)b * a.hkv + h_kv) * a.n_splits) * a.rows + r;
   const size_t sstride = (size_t)a.rows * D;
-  const float* po = a.part_o + prow0 * D + PER * lane;
+  const int col = 64 * ch + lane;
+  const float* po = a.part_o + prow0 * D + col;
   const int ns = a.n_splits;
 
   // lane s holds split s's log-sum-exp (n_splits <= 64)
   const float ls = lane < ns ? a.part_lse[prow0 + (size_t)lane * a.rows] : -__builtin_inff();
-  fv_t x[MB];
+  float x[MB];
 #pragma unroll
   for (int u = 0; u < MB; ++u)
-    if (u < ns) x[u] = *reinterpret_cast<const fv_t*>(po + (size_t)u * sstride);
+    if (u < ns) x[u] = po[(size_t)u * sstride];
   const float mt = wave_max(ls);
   const float w = ls == -__builtin_inff() ? 0.f : fast_exp2(ls - mt);
   const float wsum = wave_sum(w);
@@ -397,7 +399,7 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), sidx));
   };
 
-  fv_t acc = {};
+  float acc = 0.f;
   // an empty split (weight 0) holds zeros; its data is never multiplied
 #pragma unroll
   for (int u = 0; u < MB; ++u) {
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   for (int s0 = MB; s0 < ns; s0 += MB) {
 #pragma unroll
     for (int u = 0; u < MB; ++u)
-      if (s0 + u < ns) x[u] = *reinterpret_cast<const fv_t*>(po + (size_t)(s0 + u) * sstride);
+      if (s0 + u < ns) x[u] = po[(size_t)(s0 + u) * sstride];
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
       if (s0 + u < ns) {
@@ -418,16 +420,12 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
       }
     }
   }
-  const float sc = wsum > 0.f ? a.v_scale / wsum : 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float v = acc[e] * sc;
-    if constexpr (QDT == DT_F32)
-      reinterpret_cast<float*>(a.o)[qrow * D + PER * lane + e] = v;
-    else
-      reinterpret_cast<__bf16*>(a.o)[qrow * D + PER * lane + e] = (__bf16)v;
-  }
-  if (lane == 0) a.lse[qrow] = wsum > 0.f ? (mt + fast_log2(wsum)) * kLn2 : -__builtin_inff();
+  const float v = acc * (wsum > 0.f ? a.v_scale / wsum : 0.f);
+  if constexpr (QDT == DT_F32)
+    reinterpret_cast<float*>(a.o)[qrow * D + col] = v;
+  else
+    reinterpret_cast<__bf16*>(a.o)[qrow * D + col] = (__bf16)v;
+  if (ch == 0 && lane == 0) a.lse[qrow] = wsum > 0.f ? (mt + fast_log2(wsum)) * kLn2 : -__builtin_inff();
 }
 
 template <int D, int KDT>
@@ -440,7 +438,7 @@ int launch_t(const PagedArgs& a, int64_t n_blocks, hipStream_t s) {
 
 template <int D>
 int launch_merge_t(const PagedArgs& a, int q_dtype, hipStream_t s) {
-  const int64_t waves = (int64_t)a.batch * a.hkv * a.rows;
+  const int64_t waves = (int64_t)a.batch * a.hkv * a.rows * (D / 64);
   const int64_t blocks = (waves + 3) / 4;
   if (blocks == 0) return 0;
   if (q_dtype == DT_F32)

@@ -154,6 +154,9 @@ def test_verify_gqa_ratios(gpu_lib, hq, hkv):
     ([900, 2049], 16, 4, 4, 64, FP8),                 # fp8, D = 64, 16-token draft, G = 1
     ([4100], 4, 8, 2, 256, FP8),                      # fp8, D = 256, 16 stacked rows
     ([333, 16, 15], 16, 2, 2, 128, BF16),             # 16-token draft, one full / partial page
+    ([3000, 70, 0], 8, 16, 4, 128, BF16),             # 32 stacked rows, short and empty prefixes
+    ([1000, 4097], 6, 16, 2, 64, FP8),                # fp8, D = 64, 48 stacked rows
+    ([2500, 63], 16, 8, 2, 128, FP8),                 # fp8, 64 stacked rows, 16-token draft
 ])
 def test_verify_edge_cases(gpu_lib, prefix_lens, lx, hq, hkv, d, kvdt):
     n_pages = int(sum((x + 15) // 16 for x in prefix_lens)) + 7
