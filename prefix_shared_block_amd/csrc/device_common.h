@@ -90,6 +90,44 @@ __device__ __forceinline__ float load_elem(const void* base, size_t idx) {
   }
 }
 
+// LDS byte address of a __shared__ object (32-bit, as the DS and M0 forms take)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// One wave-wide 16-byte-per-lane copy global -> LDS: lane l's 16 bytes land
+// at LDS address lds + 16 * l.  Issued in asm so that the compiler does not
+// fence every later LDS read on it; completion is awaited with wait_vmcnt.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Cross-row swaps of gfx950 (v_permlane16_swap / v_permlane32_swap) used to
+// reach lane l ^ 16 / l ^ 32: called with the same value in both operands the
+// instruction returns (own, partner) in some order, so max(r[0], r[1]) is the
+// pair's maximum.  The two results are copied into scalars before the bit
+// cast: a bit cast applied to an element of a vector value reads element 0.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const uint32_t r0 = r[0], r1 = r[1];
+  return fmaxf(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);

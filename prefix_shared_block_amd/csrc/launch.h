@@ -51,6 +51,8 @@ struct PagedArgs {
 
 // dtype codes follow psattn_dtype (0 f32, 1 bf16, 2 fp8 e4m3fn)
 int launch_flat(const FlatArgs& a, int d, int dtype, int64_t n_blocks, void* stream);
+// bf16 flat kernel, defined in psattn_flat.hip
+int launch_flat_bf16(const FlatArgs& a, int d, int64_t n_blocks, void* stream);
 struct PagedGeom;
 int launch_paged(const PagedArgs& a, int d, int q_dtype, int kv_dtype, const PagedGeom& geo,
                  int64_t n_blocks, void* stream);

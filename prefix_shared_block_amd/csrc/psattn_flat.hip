@@ -1,0 +1,268 @@
+// psattn_flat.hip -- flat-packed prefix-shared attention forward (bf16), gfx950.
+//
+// PrefixSharing PR #50 ("设计简介", design summary) stores the shared prompt
+// once, [P | S1 | ... | SN], and lets rollout token t of segment i see the
+// prefix keys [0, P) and its own segment's keys up to t.  The planner turns
+// that visibility into work items (a tile of query tokens inside the prefix
+// or inside one rollout, stacked with the G query heads of one kv head); this
+// kernel runs one item per workgroup:
+//
+//  * 4 waves x 32 stacked query rows; Q^T fragments stay in registers;
+//  * the item's key ranges (the prefix, then the rollout's own keys) are
+//    walked in 64-key tiles.  Each tile's K and V rows are copied global ->
+//    LDS by global_load_lds_dwordx4 (no register staging, no VALU), one tile
+//    ahead of the arithmetic in a double buffer; the 16-byte chunks of a row
+//    land XOR-swizzled (the global address is permuted, the LDS side is
+//    contiguous), so the operand reads below avoid bank conflicts;
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 K rows from LDS), so a
+//    lane holds 16 scores of its own query row; online softmax in the log2
+//    domain.  The running maximum is exact (a row's largest weight is 1.0,
+//    exact in bf16, which matters for rows one outlier key dominates); the
+//    rescale of the accumulators is skipped when no row of the wave grew;
+//  * O^T += V^T P^T with P^T taken from the score registers and V^T read from
+//    the row-major V tile by ds_read_b64_tr_b16 (no transposed LDS writes).
+//    The contraction order follows the score layout: position 8 g + e of the
+//    16-key step ks is key 16 ks + 8 (e / 4) + 4 g + e % 4.
+#include "device_common.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace psattn {
+namespace {
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+
+#define PF_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+
+template <int D>
+struct F2Cfg {
+  static constexpr int BN = 64;                                   // keys per tile
+  static constexpr int ROWB = 2 * D;                              // bytes of a K (or V) row
+  static constexpr int CPR = ROWB / 16;                           // 16-byte chunks per row
+  static constexpr int TILE = BN * ROWB;                          // K (or V) tile bytes
+  static constexpr int NCOPY = TILE / 1024;                       // wave-wide 1 KiB copies per K (or V) tile
+  static constexpr int CPW = 2 * NCOPY / kWaves;                  // copies per wave per tile (K + V)
+  static constexpr int NSTEP = D / 16;                            // k-steps of the score product
+  static constexpr int NDB = D / 32;                              // 32-column output blocks
+  static constexpr int MINB = D >= 256 ? 1 : 2;
+  static_assert(2 * NCOPY % kWaves == 0, "copies split evenly over the waves");
+  __device__ static constexpr int fk(int r) { return r & (CPR - 1); }
+  __device__ static constexpr int fv(int r) { return (2 * r) & (CPR - 1); }
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F2Cfg<D>::MINB)))
+void flat2_kernel(FlatArgs a) {
+  using C = F2Cfg<D>;
+  constexpr int BN = C::BN;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][C::TILE];  // [buffer][K, V]
+
+  const int blk = blockIdx.x;
+  const int h_kv = blk % a.hkv;
+  const int j = blk / a.hkv;
+  const Item it = flat_item(j, h_kv, a.prefix_len, a.nseg, a.seg_offsets, a.tile_tokens);
+  if (it.kind == kNone) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  // stacked row of this lane's query column: token-major, heads interleaved
+  const int r = wave * kWaveRows + l32;
+  const int tok = r / a.g;
+  const int hl = r - tok * a.g;
+  const int token = it.q_begin + tok;
+  const bool valid = (tok < a.tile_tokens) && (token < it.q_end);
+  const int token_c = valid ? token : it.q_begin;
+  const size_t qrow = (size_t)token_c * a.hq + h_kv * a.g + hl;
+
+  // Q^T fragments: k-step s, lane group g holds d = 16 s + 8 g .. +8
+  bf16x8_t qf[C::NSTEP];
+  {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
+#pragma unroll
+    for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * s + 8 * g);
+  }
+
+  const int n0 = cdiv32(it.r0_end - it.r0_begin, BN);
+  const int n1 = cdiv32(it.r1_end - it.r1_begin, BN);
+  const int nt = n0 + n1;
+  auto tile_range = [&](int n, int& k0, int& ke) {
+    if (n < n0) {
+      k0 = it.r0_begin + n * BN;
+      ke = it.r0_end;
+    } else {
+      k0 = it.r1_begin + (n - n0) * BN;
+      ke = it.r1_end;
+    }
+  };
+
+  const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h_kv * C::ROWB;
+  const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)h_kv * C::ROWB;
+  const size_t row_stride = (size_t)a.hkv * C::ROWB;
+
+  // this wave's share of the copies of tile n into buffer bsel; rows past
+  // the range end repeat its last row (finite data, masked below)
+  auto issue = [&](int n, int bsel) {
+    int k0, ke;
+    tile_range(n, k0, ke);
+#pragma unroll
+    for (int t = 0; t < C::CPW; ++t) {
+      const int q = wave * C::CPW + t;
+      const bool isv = q >= C::NCOPY;
+      const int jb = isv ? q - C::NCOPY : q;
+      const int p = jb * 64 + lane;
+      const int row = p / C::CPR;
+      const int pos = p % C::CPR;
+      int key = k0 + row;
+      key = key < ke ? key : ke - 1;
+      const char* src = (isv ? vbase : kbase) + (size_t)key * row_stride +
+                        16 * (pos ^ (isv ? C::fv(row) : C::fk(row)));
+      dma16(src, lds_addr(&smem[bsel][isv ? 1 : 0][jb * 1024]));
+    }
+  };
+
+  float m_run = kNegBig;
+  float l_run = 0.f;
+  f32x16_t o[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  const float c = a.scale_log2;
+
+  auto math = [&](const char* kt, const char* vt, int key0, int kend, bool needmask) {
+    // ---- S^T for keys 32 kb + (0..31): lane (l32, g), reg i holds key
+    // 32 kb + 8 (i / 4) + 4 g + i % 4 of query row l32
+    f32x16_t sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+      const int row = 32 * kb + l32;
+      const char* krow = kt + row * C::ROWB;
+#pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((2 * s + g) ^ C::fk(row)));
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kb], 0, 0, 0);
+      }
+    }
+    float mr = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = sc[kb][i];
+        if (needmask) {
+          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key >= kend || key > token) x = -__builtin_inff();
+        }
+        sc[kb][i] = x;
+        mr = fmaxf(mr, x);
+      }
+    mr = max_xor32(mr);
+    const float mx = mr * c;
+    const bool grow = mx > m_run;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mn = grow ? mx : m_run;
+      const float al = fast_exp2(m_run - mn);
+      l_run *= al;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= al;
+      m_run = mn;
+    }
+    bf16x8_t pt[4];  // k-step ks = 2 kb + half: regs 8 half .. 8 half + 7 of sc[kb]
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_run));
+        pt[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+        psum += p;
+      }
+    l_run += psum;
+    // ---- O^T += V^T P^T: A operand lane (d, g) = V rows 16 ks + 8 t + 4 g + 0..3
+    // of column d (t = 0, 1), by ds_read_b64_tr_b16: in-group source lane
+    // ap + 4 sp addresses row 16 ks + 8 t + 4 g + sp, columns 4 ap .. +3
+    const int li = lane & 15;
+    const int sp = li >> 2;
+    const int ap = li & 3;
+    const int hgrp = l32 >> 4;
+#pragma unroll
+    for (int ks = 0; ks < BN / 16; ++ks) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        s16x4_t vv[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int row = 16 * ks + 8 * t + 4 * g + sp;
+          const int chunk = 4 * db + 2 * hgrp + (ap >> 1);
+          vv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              PF_LDS_PTR(s16x4_t, vt + row * C::ROWB + 16 * (chunk ^ C::fv(row)) + 8 * (ap & 1)));
+        }
+        const s16x8_t v8 = {vv[0][0], vv[0][1], vv[0][2], vv[0][3], vv[1][0], vv[1][1], vv[1][2], vv[1][3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v8), pt[ks], o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // retire the query loads before the copies start: the copies are waited for
+  // with explicit vmcnt counts that the compiler does not know about
+#pragma unroll
+  for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(qf[s]));
+  if (nt > 0) issue(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int n = 0; n < nt; ++n) {
+    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+    int k0, ke;
+    tile_range(n, k0, ke);
+    const bool needmask = (k0 + BN > ke) || (k0 + BN - 1 > it.q_begin);
+    math(smem[n & 1][0], smem[n & 1][1], k0, ke, needmask);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (valid) {
+    const size_t obase = qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * g;
+        const u32x2_t v = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                           pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.o) + obase + d) = v;
+      }
+    }
+    if (g == 0) a.lse[qrow] = (m_run + fast_log2(lt)) * kLn2;
+  }
+}
+
+template <int D>
+int launch_t(const FlatArgs& a, int64_t n_blocks, hipStream_t s) {
+  hipLaunchKernelGGL((flat2_kernel<D>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_flat_bf16(const FlatArgs& a, int d, int64_t n_blocks, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (d) {
+    case 64: return launch_t<64>(a, n_blocks, s);
+    case 128: return launch_t<128>(a, n_blocks, s);
+    case 256: return launch_t<256>(a, n_blocks, s);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace psattn

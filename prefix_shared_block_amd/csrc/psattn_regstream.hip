@@ -77,18 +77,6 @@ struct RCfg {
   __device__ static constexpr int fv(int r) { return (2 * r) & (TCPR - 1); }
 };
 
-// max of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lane
-// groups holding one query row's scores) with the gfx950 cross-row swaps:
-// permlane{16,32}_swap(x, x) returns this lane's value and its partner's
-__device__ __forceinline__ float max_over_groups(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t w = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
-}
-
 // 16 bytes of a global row (chunk pos) -> the row's LDS tile slot(s), as bf16
 template <int KDT, int TCPR>
 __device__ __forceinline__ void put_chunk(char* trow, int pos, int f, const u32x4_t x) {
@@ -247,7 +235,7 @@ void paged_reg_kernel(PagedArgs a) {
       sc[e] = x;
       mr = fmaxf(mr, x);
     }
-    mr = max_over_groups(mr);
+    mr = max_xor32(max_xor16(mr));  // the row's four lane groups
     const float mx = mr * c;
     const bool grow = mx > m_run + kTau;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {

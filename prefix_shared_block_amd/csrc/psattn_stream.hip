@@ -46,25 +46,6 @@ typedef int i32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kTau = 8.0f;  // lazy-rescale threshold (log2 units)
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// One wave-wide 16-byte-per-lane copy global -> LDS: lane l's 16 bytes land
-// at LDS address lds + 16 * l.  Issued in asm so that the compiler does not
-// fence every later LDS read on it; completion is awaited with wait_vmcnt.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds))
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ bf16x8_t fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   u32x4_t r;
   r[0] = fp8x2_to_bf16x2<false>(w0);

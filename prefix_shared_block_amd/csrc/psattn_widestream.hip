@@ -83,16 +83,6 @@ __device__ __forceinline__ void wput(char* trow, int pos, int f, const u32x4_t x
   }
 }
 
-// max of x over the lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row's scores)
-__device__ __forceinline__ float wmax_over_groups(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float y = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
-  const uint32_t w = __builtin_bit_cast(uint32_t, y);
-  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
-}
-
 template <int D, int KDT>
 __global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_wide_kernel(PagedArgs a) {
@@ -239,7 +229,7 @@ void paged_wide_kernel(PagedArgs a) {
         sc[j][e] = x;
         mr = fmaxf(mr, x);
       }
-    mr = wmax_over_groups(mr);
+    mr = max_xor32(max_xor16(mr));  // the row's four lane groups
     const float mx = mr * c;
     const bool grow = mx > m_run + kTau;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {

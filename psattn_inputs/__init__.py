@@ -257,6 +257,46 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
 
 
 # ---------------------------------------------------------------------------
+# spike inputs: every query non-negative and a few key rows set to +16 in
+# every element, so that a query's score for a spike key exceeds its other
+# scores by far more than 128 ln 2 (a softmax that lost track of its row
+# maximum overflows on these).  Bit-level edits only.
+# ---------------------------------------------------------------------------
+def _abs_bits(x: np.ndarray, dt: int) -> np.ndarray:
+    if dt == F32:
+        return np.abs(x)
+    if dt == BF16:
+        return x & np.uint16(0x7FFF)
+    raise ValueError(dt)
+
+
+def make_flat_spikes(prefix_len: int, seg_lens: Sequence[int], hq: int, hkv: int, d: int,
+                     spikes: Sequence[int], dtype: int = BF16, seed: int = 0,
+                     name: str = "flat_spikes") -> FlatInstance:
+    inst = make_flat(prefix_len, seg_lens, hq, hkv, d, dtype=dtype, seed=seed, name=name)
+    inst.q = _abs_bits(inst.q, dtype)
+    for t in spikes:
+        inst.k[t] = _encode(np.full((hkv, d), 16.0, np.float32), dtype)
+    return inst
+
+
+def make_paged_spikes(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d: int,
+                      spikes: Sequence[int], kv_dtype: int = BF16, seed: int = 0,
+                      num_pages: Optional[int] = None, name: str = "paged_spikes") -> PagedInstance:
+    """Spikes at the given prefix positions of every request that has them."""
+    inst = make_paged(prefix_lens, draft_len, hq, hkv, d, kv_dtype=kv_dtype, seed=seed,
+                      num_pages=num_pages, scales=(kv_dtype == FP8), name=name)
+    inst.q = _abs_bits(inst.q, inst.q_dtype)
+    row = _encode(np.full((hkv, d), 16.0, np.float32), kv_dtype)
+    for b, pl in enumerate(inst.prefix_lens):
+        for t in spikes:
+            if t < pl:
+                page = inst.kv_indices[inst.kv_indptr[b] + t // PAGE_SIZE]
+                inst.k_pool[page, t % PAGE_SIZE] = row
+    return inst
+
+
+# ---------------------------------------------------------------------------
 # the five named workloads
 # ---------------------------------------------------------------------------
 CONFIG_NAMES = ["tiny", "grpo", "verify16k", "verify_fp8", "grpo_ragged"]

@@ -13,7 +13,8 @@ import pytest
 
 from gpu_util import compare, kind_of, run_flat, run_paged, sample_rows as _sample_rows, to_f64
 from oracle.attention import attn_flat, attn_paged
-from psattn_inputs import BF16, F32, FP8, make_config, make_flat, make_flat_random_lens, make_paged
+from psattn_inputs import (BF16, F32, FP8, make_config, make_flat, make_flat_random_lens, make_flat_spikes,
+                           make_paged, make_paged_spikes)
 
 pytestmark = pytest.mark.gpu
 
@@ -163,6 +164,29 @@ def test_verify_edge_cases(gpu_lib, prefix_lens, lx, hq, hkv, d, kvdt):
     inst = make_paged(prefix_lens, lx, hq, hkv, d, kv_dtype=kvdt, seed=sum(prefix_lens) % 1000,
                       num_pages=n_pages, scales=(kvdt == FP8))
     _paged_check(gpu_lib, inst, label=f"verify {prefix_lens} Lx={lx} {hq}/{hkv} D={d}")
+
+
+# Spike keys dominate every query that sees them by more than 128 ln 2, at
+# positions spread over tiles, stages and lane groups: a row maximum that
+# missed any lane's scores would overflow the softmax weights here.
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_flat_spike_keys(gpu_lib, d):
+    inst = make_flat_spikes(300, [130, 70], 8, 2, d, spikes=[3, 21, 40, 62, 104, 126, 190, 250, 317, 345, 439],
+                            seed=40 + d)
+    _flat_check(gpu_lib, inst, label=f"flat spikes D={d}")
+
+
+@pytest.mark.parametrize("lx,hq,hkv,d,kvdt", [
+    (4, 8, 2, 128, BF16),    # 16 stacked rows
+    (2, 8, 2, 256, FP8),     # 8 stacked rows, fp8
+    (8, 16, 2, 128, BF16),   # 64 stacked rows
+    (8, 8, 2, 256, FP8),     # 32 stacked rows, fp8
+])
+def test_verify_spike_keys(gpu_lib, lx, hq, hkv, d, kvdt):
+    spikes = [5, 18, 31, 37, 58, 63, 700, 1023, 1500, 2047]
+    inst = make_paged_spikes([2100, 900, 40], lx, hq, hkv, d, spikes=spikes, kv_dtype=kvdt, seed=50 + d,
+                             num_pages=200)
+    _paged_check(gpu_lib, inst, label=f"verify spikes Lx={lx} {hq}/{hkv} D={d}")
 
 
 def test_verify_zero_queries_closed_form(gpu_lib):
