@@ -276,7 +276,7 @@ def main():
     g_flops = flat_useful_flops(g_inst)
     g_tflops = g_flops / (tg["mean"] * 1e-3) / 1e12
     g_tflops_best = g_flops / (tg["min"] * 1e-3) / 1e12
-    traffic = traffic_from_profile("flat_fwd_kernel<128, false>", grpo.grid_threads())
+    traffic = traffic_from_profile("flat2_kernel<128>", grpo.grid_threads())
     out = {
         "metric": METRIC,
         "value": round(g_tflops, 2),
@@ -294,7 +294,7 @@ def main():
                    "global_batch": 8, "seq_len": 2048 + 512, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "flat_fwd_kernel<128,bf16>",
+                     "traffic": traffic, "kernel": "flat2_kernel<128> (bf16)",
                      "per_launch_useful_flop": g_flops, "best_call_tflops": round(g_tflops_best, 2)},
         "grpo_hbm_gbs": round(flat_alg_bytes(g_inst) / (tg["mean"] * 1e-3) / 1e9, 1),
     }
