@@ -272,6 +272,32 @@ def test_paged_zero_prefix_is_draft_causal():
         assert np.max(np.abs(o[sl] - ro)) <= 1e-12 and np.max(np.abs(lse[sl] - rl)) <= 1e-12
 
 
+@pytest.mark.parametrize("cuts", [[0, 7, 7, 40, 64], [0, 1, 2, 64], [0, 33, 64]])
+def test_split_merge_equals_unsplit(cuts):
+    """Associativity of the log-sum-exp: attention over arbitrary key splits
+    (including an empty one) merged with O = sum_s e^(LSE_s - LSE) O_s,
+    LSE = log sum_s e^LSE_s equals attention over all keys at once."""
+    rng = np.random.default_rng(31)
+    L, hq, hkv, d = 64, 6, 2, 8
+    kx = rng.standard_normal((L, hkv, d))
+    vx = rng.standard_normal((L, hkv, d))
+    qr = rng.standard_normal((5, hq, d))
+    qpos = np.full(5, L - 1)
+    o_all, l_all = causal_attention(qr, qpos, kx, vx, 0.3)
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        if b > a:
+            parts.append(causal_attention(qr, np.full(5, b - a - 1), kx[a:b], vx[a:b], 0.3))
+        else:
+            parts.append((np.zeros_like(o_all), np.full(l_all.shape, -np.inf)))  # empty split
+    lses = np.stack([p[1] for p in parts])
+    lse = np.logaddexp.reduce(lses, axis=0)
+    w = np.exp(lses - lse[None])
+    o = np.einsum("shr,shrd->hrd", w.transpose(0, 2, 1), np.stack([p[0] for p in parts]).transpose(0, 2, 1, 3))
+    assert np.allclose(lse, l_all, atol=1e-12, rtol=0)
+    assert np.allclose(o.transpose(1, 0, 2), o_all, atol=1e-12, rtol=0)
+
+
 def test_causal_attention_rejects_bad_heads():
     with pytest.raises(ValueError):
         causal_attention(np.zeros((1, 3, 2)), np.array([0]), np.zeros((1, 2, 2)), np.zeros((1, 2, 2)), 1.0)
