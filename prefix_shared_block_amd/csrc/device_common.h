@@ -105,6 +105,16 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
+// The same copy with a wave-uniform 64-bit base in scalar registers and a
+// 32-bit per-lane byte offset (the saddr form: no 64-bit address arithmetic
+// per lane).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

@@ -27,6 +27,8 @@
 #include "launch.h"
 #include "plan.h"
 
+#include <type_traits>
+
 namespace psattn {
 namespace {
 
@@ -91,7 +93,7 @@ void flat2_kernel(FlatArgs a) {
   const int n0 = cdiv32(it.r0_end - it.r0_begin, BN);
   const int n1 = cdiv32(it.r1_end - it.r1_begin, BN);
   const int nt = n0 + n1;
-  auto tile_range = [&](int n, int& k0, int& ke) {
+  auto tile_range = [&](int n, int& k0, int& ke) __attribute__((always_inline)) {
     if (n < n0) {
       k0 = it.r0_begin + n * BN;
       ke = it.r0_end;
@@ -103,26 +105,48 @@ void flat2_kernel(FlatArgs a) {
 
   const char* kbase = reinterpret_cast<const char*>(a.k) + (size_t)h_kv * C::ROWB;
   const char* vbase = reinterpret_cast<const char*>(a.v) + (size_t)h_kv * C::ROWB;
-  const size_t row_stride = (size_t)a.hkv * C::ROWB;
+  const uint32_t row_stride = (uint32_t)a.hkv * C::ROWB;
 
-  // this wave's share of the copies of tile n into buffer bsel; rows past
-  // the range end repeat its last row (finite data, masked below)
-  auto issue = [&](int n, int bsel) {
+  // This wave's copies of a tile: copy q = wave * CPW + t is 1 KiB block jb of
+  // the K tile (q < NCOPY) or of the V tile.  Lane l of a block carries chunk
+  // pos of tile row `row` (p = 64 jb + l); its byte offset inside the tile's
+  // rows is fixed, so it is computed once.
+  const bool w_isv = wave * C::CPW >= C::NCOPY;  // a wave's copies are all K or all V
+  const char* wbase = w_isv ? vbase : kbase;
+  uint32_t coff[C::CPW];
+#pragma unroll
+  for (int t = 0; t < C::CPW; ++t) {
+    const int jb = (wave * C::CPW + t) % C::NCOPY;
+    const int p = jb * 64 + lane;
+    const int row = p / C::CPR;
+    const int pos = p % C::CPR;
+    coff[t] = (uint32_t)row * row_stride + 16u * (uint32_t)(pos ^ (w_isv ? C::fv(row) : C::fk(row)));
+  }
+  // copies of tile n into LDS buffer B; rows past the range end repeat its
+  // last row (finite data, masked in the arithmetic)
+  auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
+    const uint32_t bofs = (uint32_t)bsel * (2 * C::TILE);
     int k0, ke;
     tile_range(n, k0, ke);
+    const char* base = wbase + (size_t)k0 * row_stride;
+    if (k0 + BN <= ke) {
 #pragma unroll
-    for (int t = 0; t < C::CPW; ++t) {
-      const int q = wave * C::CPW + t;
-      const bool isv = q >= C::NCOPY;
-      const int jb = isv ? q - C::NCOPY : q;
-      const int p = jb * 64 + lane;
-      const int row = p / C::CPR;
-      const int pos = p % C::CPR;
-      int key = k0 + row;
-      key = key < ke ? key : ke - 1;
-      const char* src = (isv ? vbase : kbase) + (size_t)key * row_stride +
-                        16 * (pos ^ (isv ? C::fv(row) : C::fk(row)));
-      dma16(src, lds_addr(&smem[bsel][isv ? 1 : 0][jb * 1024]));
+      for (int t = 0; t < C::CPW; ++t) {
+        const int jb = (wave * C::CPW + t) % C::NCOPY;
+        dma16_s(base, coff[t], lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
+      }
+    } else {
+      const int lastr = ke - 1 - k0;
+#pragma unroll
+      for (int t = 0; t < C::CPW; ++t) {
+        const int jb = (wave * C::CPW + t) % C::NCOPY;
+        const int p = jb * 64 + lane;
+        const int row = p / C::CPR;
+        const int pos = p % C::CPR;
+        const int rc = row < lastr ? row : lastr;
+        const uint32_t off = (uint32_t)rc * row_stride + 16u * (uint32_t)(pos ^ (w_isv ? C::fv(row) : C::fk(row)));
+        dma16_s(base, off, lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
+      }
     }
   };
 
@@ -135,7 +159,9 @@ void flat2_kernel(FlatArgs a) {
     for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
   const float c = a.scale_log2;
 
-  auto math = [&](const char* kt, const char* vt, int key0, int kend, bool needmask) {
+  // MASK: the tile crosses the range end or the causal diagonal
+  auto math = [&](const char* kt, const char* vt, int key0, int kend, auto maskc) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(maskc)::value;
     // ---- S^T for keys 32 kb + (0..31): lane (l32, g), reg i holds key
     // 32 kb + 8 (i / 4) + 4 g + i % 4 of query row l32
     f32x16_t sc[2];
@@ -152,18 +178,21 @@ void flat2_kernel(FlatArgs a) {
       }
     }
     float mr = -__builtin_inff();
+    if constexpr (MASK) {
+      // visible keys of this row: key < kend and key <= token
+      const int lim = (kend < token + 1 ? kend : token + 1) - key0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kr = 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+          sc[kb][i] = kr < lim ? sc[kb][i] : -__builtin_inff();
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = sc[kb][i];
-        if (needmask) {
-          const int key = key0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= kend || key > token) x = -__builtin_inff();
-        }
-        sc[kb][i] = x;
-        mr = fmaxf(mr, x);
-      }
+      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[kb][i]);
     mr = max_xor32(mr);
     const float mx = mr * c;
     const bool grow = mx > m_run;
@@ -211,6 +240,16 @@ void flat2_kernel(FlatArgs a) {
     }
   };
 
+  auto compute = [&](int n) __attribute__((always_inline)) {
+    int k0, ke;
+    tile_range(n, k0, ke);
+    const bool needmask = (k0 + BN > ke) || (k0 + BN - 1 > it.q_begin);
+    const char* kt = smem[n & 1][0];
+    const char* vt = smem[n & 1][1];
+    (void)needmask;
+    math(kt, vt, k0, ke, std::true_type{});
+  };
+
   // retire the query loads before the copies start: the copies are waited for
   // with explicit vmcnt counts that the compiler does not know about
 #pragma unroll
@@ -220,10 +259,7 @@ void flat2_kernel(FlatArgs a) {
   __syncthreads();
   for (int n = 0; n < nt; ++n) {
     if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    int k0, ke;
-    tile_range(n, k0, ke);
-    const bool needmask = (k0 + BN > ke) || (k0 + BN - 1 > it.q_begin);
-    math(smem[n & 1][0], smem[n & 1][1], k0, ke, needmask);
+    compute(n);
     wait_vmcnt<0>();
     __syncthreads();
   }
