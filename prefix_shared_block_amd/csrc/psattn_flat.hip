@@ -90,12 +90,29 @@ void flat2_kernel(FlatArgs a) {
     for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * s + 8 * g);
   }
 
+  // Tiles of a range that are whole and end at or before the item's first
+  // query token are visible to every row: they form a leading run of the
+  // range.  They are walked first (no mask), then the rest of both ranges.
   const int n0 = cdiv32(it.r0_end - it.r0_begin, BN);
   const int n1 = cdiv32(it.r1_end - it.r1_begin, BN);
   const int nt = n0 + n1;
+  auto n_clean = [&](int b, int e) __attribute__((always_inline)) {
+    const int whole = (e - b) / BN;
+    const int causal = it.q_begin + 1 - b >= 0 ? (it.q_begin + 1 - b) / BN : 0;
+    return whole < causal ? whole : causal;
+  };
+  const int c0 = n0 > 0 ? n_clean(it.r0_begin, it.r0_end) : 0;
+  const int c1 = n1 > 0 ? n_clean(it.r1_begin, it.r1_end) : 0;
+  const int nc = c0 + c1;
   auto tile_range = [&](int n, int& k0, int& ke) __attribute__((always_inline)) {
-    if (n < n0) {
+    if (n < c0) {
       k0 = it.r0_begin + n * BN;
+      ke = it.r0_end;
+    } else if (n < nc) {
+      k0 = it.r1_begin + (n - c0) * BN;
+      ke = it.r1_end;
+    } else if (n < nc + n0 - c0) {
+      k0 = it.r0_begin + (n - c1) * BN;
       ke = it.r0_end;
     } else {
       k0 = it.r1_begin + (n - n0) * BN;
@@ -240,14 +257,10 @@ void flat2_kernel(FlatArgs a) {
     }
   };
 
-  auto compute = [&](int n) __attribute__((always_inline)) {
+  auto compute = [&](int n, auto maskc) __attribute__((always_inline)) {
     int k0, ke;
     tile_range(n, k0, ke);
-    const bool needmask = (k0 + BN > ke) || (k0 + BN - 1 > it.q_begin);
-    const char* kt = smem[n & 1][0];
-    const char* vt = smem[n & 1][1];
-    (void)needmask;
-    math(kt, vt, k0, ke, std::true_type{});
+    math(smem[n & 1][0], smem[n & 1][1], k0, ke, maskc);
   };
 
   // retire the query loads before the copies start: the copies are waited for
@@ -257,9 +270,16 @@ void flat2_kernel(FlatArgs a) {
   if (nt > 0) issue(0, 0);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int n = 0; n < nt; ++n) {
+  int n = 0;
+  for (; n < nc; ++n) {
     if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    compute(n);
+    compute(n, std::false_type{});
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  for (; n < nt; ++n) {
+    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+    compute(n, std::true_type{});
     wait_vmcnt<0>();
     __syncthreads();
   }
