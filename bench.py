@@ -96,7 +96,7 @@ class FlatRunner:
         d = self.ps.flat_desc(self.inst.total_tokens, self.inst.prefix_len, self.inst.num_segments,
                               self.seg.data_ptr(), self.inst.max_seg_len)
         info = self.ps.plan_info(d, self.inst.hq, self.inst.hkv, self.inst.d, self.inst.dtype, self.inst.dtype)
-        return int(info.n_items) * 256
+        return int(info.n_items) * (int(info.rows_per_tile) // 32) * 64
 
     def __call__(self):
         self.ps.fwd_flat(self.q, self.k, self.v, self.inst.prefix_len, self.seg, self.inst.max_seg_len,

@@ -16,9 +16,8 @@
 //    contiguous), so the operand reads below avoid bank conflicts;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 K rows from LDS), so a
 //    lane holds 16 scores of its own query row; online softmax in the log2
-//    domain.  The running maximum is exact (a row's largest weight is 1.0,
-//    exact in bf16, which matters for rows one outlier key dominates); the
-//    rescale of the accumulators is skipped when no row of the wave grew;
+//    domain.  The reference maximum is moved lazily (see kTauFlat), and the
+//    rescale of the accumulators is skipped when no row of the wave moved;
 //  * O^T += V^T P^T with P^T taken from the score registers and V^T read from
 //    the row-major V tile by ds_read_b64_tr_b16 (no transposed LDS writes).
 //    The contraction order follows the score layout: position 8 g + e of the
@@ -38,6 +37,12 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 #define PF_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 
+// Lazy rescale: a row moves its reference maximum only when a tile's
+// maximum exceeds it by more than kTauFlat (log2 units), so the weights stay
+// <= 2^kTauFlat and the rescale of O (wave-wide, skipped unless some row
+// moved) is rare after the first tiles.
+constexpr float kTauFlat = 8.0f;
+
 template <int D>
 struct F2Cfg {
   static constexpr int BN = 64;                                   // keys per tile
@@ -51,7 +56,10 @@ struct F2Cfg {
   static constexpr int MINB = D >= 256 ? 1 : 2;
   static_assert(2 * NCOPY % kWaves == 0, "copies split evenly over the waves");
   __device__ static constexpr int fk(int r) { return r & (CPR - 1); }
-  __device__ static constexpr int fv(int r) { return (2 * r) & (CPR - 1); }
+  // V rows: a 32-lane pass of the transposed reads covers 4 rows x 4 chunks;
+  // the swizzle spreads them over all 64 banks (rows of 128 bytes already
+  // alternate bank halves, so there only row pairs are separated)
+  __device__ static constexpr int fv(int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 template <int D>
@@ -212,7 +220,7 @@ void flat2_kernel(FlatArgs a) {
       for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[kb][i]);
     mr = max_xor32(mr);
     const float mx = mr * c;
-    const bool grow = mx > m_run;
+    const bool grow = mx > m_run + kTauFlat;
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float mn = grow ? mx : m_run;
       const float al = fast_exp2(m_run - mn);
