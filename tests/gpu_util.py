@@ -66,7 +66,7 @@ def run_flat(lib, inst, dev="cuda"):
     return o, lse
 
 
-def run_paged(lib, inst, dev="cuda"):
+def run_paged(lib, inst, dev="cuda", workspace=None):
     import torch
 
     q = to_dev(inst.q, inst.q_dtype, dev)
@@ -82,7 +82,7 @@ def run_paged(lib, inst, dev="cuda"):
     lse, lf = guarded_empty((q.shape[0], q.shape[1]), torch.float32, dev)
     lib.fwd_paged(q, kp, vp, indptr, indices, plens, kx, vx, inst.draft_len, inst.max_prefix_len,
                   sm_scale=inst.sm_scale, k_scale=inst.k_scale, v_scale=inst.v_scale,
-                  kv_dtype=inst.kv_dtype, out=o, lse=lse)
+                  kv_dtype=inst.kv_dtype, out=o, lse=lse, workspace=workspace)
     torch.cuda.synchronize()
     assert guards_intact(of) and guards_intact(lf), "write outside the output tensors"
     return o, lse

@@ -189,6 +189,40 @@ def test_verify_spike_keys(gpu_lib, lx, hq, hkv, d, kvdt):
     _paged_check(gpu_lib, inst, label=f"verify spikes Lx={lx} {hq}/{hkv} D={d}")
 
 
+def test_verify_workspace_reused_across_calls(gpu_lib):
+    """One workspace serves a series of calls of different shapes, split
+    counts and kernels (register streaming, wide, fp8): nothing a call leaves
+    in it may leak into the next result."""
+    import torch
+
+    def mk(plens, lx, hq, hkv, d, kvdt, seed):
+        n_pages = int(sum((x + 15) // 16 for x in plens)) + 5
+        return make_paged(plens, lx, hq, hkv, d, kv_dtype=kvdt, seed=seed, num_pages=n_pages,
+                          scales=(kvdt == FP8))
+
+    cases = [mk([1500] * 8, 4, 8, 4, 128, BF16, 61),
+             mk([3000, 70, 0], 8, 16, 4, 128, BF16, 62),
+             mk([900, 2000, 40, 600] * 4, 4, 16, 8, 128, FP8, 63),
+             mk([5000, 33], 2, 8, 2, 256, FP8, 64),
+             mk([1200, 800] * 6, 4, 4, 4, 64, BF16, 65),
+             mk([1500] * 8, 4, 8, 4, 128, BF16, 66)]
+    sizes = []
+    for inst in cases:
+        desc = gpu_lib.paged_desc(len(inst.prefix_lens), inst.draft_len, 16, inst.k_pool.shape[0], 1, 1, 1,
+                                  inst.max_prefix_len, 1, 1)
+        sizes.append(gpu_lib.psattn_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype,
+                                                   inst.kv_dtype))
+    ws = torch.full((max(sizes),), 0x7F, dtype=torch.uint8, device="cuda")  # non-zero start
+    for inst in cases:
+        o, lse = run_paged(gpu_lib, inst, workspace=ws)
+        ro, rl = attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr, inst.kv_indices,
+                            inst.prefix_lens, inst.k_ext, inst.v_ext, inst.draft_len, inst.sm_scale,
+                            k_scale=inst.k_scale, v_scale=inst.v_scale, q_dtype=inst.q_dtype,
+                            kv_dtype=inst.kv_dtype)
+        compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype),
+                f"reused workspace {list(inst.prefix_lens)[:4]} Lx={inst.draft_len} D={inst.d}")
+
+
 def test_verify_zero_queries_closed_form(gpu_lib):
     inst = make_paged([100, 0, 63], 4, 8, 2, 128, kv_dtype=BF16, seed=7, num_pages=20)
     inst.q[:] = 0
