@@ -240,6 +240,38 @@ def traffic_from_profile(kernel_prefix: str, grid: int):
     return None
 
 
+def prefix_sweep(ps, flush, calls: int, copy_calib: bool):
+    """The GRPO shape with N = 1, 2, 4, 8, 16 rollouts of 512 tokens (P = 2048,
+    Hq = 32, Hkv = 8, D = 128, bf16): a few evicted calls each, for a counter
+    run that checks that the prefix K/V is read about once per call whatever
+    N is.  Prints one JSON line with, per N, the launch grid (to match the
+    counter rows) and the algorithmic bytes split into Q, prefix K/V and
+    rollout K/V."""
+    import torch
+    from psattn_inputs import BF16, make_flat
+
+    rows = []
+    for n in (1, 2, 4, 8, 16):
+        inst = make_flat(2048, [512] * n, 32, 8, 128, dtype=BF16, seed=200 + n, name=f"grpo_n{n}")
+        run = FlatRunner(ps, inst)
+        t = time_calls(run, flush, calls, 1)
+        tok, p = inst.total_tokens, inst.prefix_len
+        rows.append({"n": n, "grid_threads": run.grid_threads(), "calls": calls + 1, "us": round(t["mean"] * 1e3, 2),
+                     "q_bytes": tok * 32 * 128 * 2, "o_bytes": tok * 32 * 128 * 2,
+                     "prefix_kv_bytes": 2 * p * 8 * 128 * 2, "rollout_kv_bytes": 2 * (tok - p) * 8 * 128 * 2})
+        del run, inst
+    out = {"prefix_sweep": rows}
+    if copy_calib:
+        n = (256 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calib_bytes"] = {"read": n * 4, "write": n * 4}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +282,8 @@ def main():
                     help="also run a plain 256 MiB device copy (known bytes) to scale profiler byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
+    ap.add_argument("--prefix-sweep", action="store_true",
+                    help="instead of the benchmark: GRPO with 1..16 rollouts, for the prefix-K/V-read-once counter check")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -263,6 +297,9 @@ def main():
     ps.load()
     torch.cuda.set_device(0)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    if args.prefix_sweep:
+        prefix_sweep(ps, flush, max(1, args.steps), args.copy_calib)
+        return
 
     log("generating grpo workload")
     g_inst = make_config("grpo")

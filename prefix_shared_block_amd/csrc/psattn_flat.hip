@@ -95,7 +95,7 @@ void flat2_kernel(FlatArgs a) {
   {
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
 #pragma unroll
-    for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * s + 8 * g);
+    for (int s = 0; s < C::NSTEP; ++s) qf[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(qp + 16 * s + 8 * g));
   }
 
   // Tiles of a range that are whole and end at or before the item's first
@@ -292,22 +292,42 @@ void flat2_kernel(FlatArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue
+  // ---- epilogue.  O = acc / l goes through LDS so that every global store
+  // is a whole 16-byte chunk of a row: the rows leave as full cache lines,
+  // written non-temporally (they are not read again here, and kept in L2 they
+  // would evict the prefix K/V the other items of this head still read).
+  // Each wave stages its 32 rows (chunk c of row r at c ^ (r % CPR)) in the
+  // tiles, which every wave is done with after the loop's last barrier.
   const float lt = l_run + __shfl_xor(l_run, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (valid) {
-    const size_t obase = qrow * D;
+  char* ost = &smem[0][0][0] + wave * (kWaveRows * C::ROWB);
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
+  for (int db = 0; db < C::NDB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * g;
-        const u32x2_t v = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
-                           pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.o) + obase + d) = v;
-      }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // columns 32 db + 8 g4 + 4 g .. +3: half g of chunk 4 db + g4
+      const u32x2_t v = {pack_bf16x2(o[db][4 * g4] * inv, o[db][4 * g4 + 1] * inv),
+                         pack_bf16x2(o[db][4 * g4 + 2] * inv, o[db][4 * g4 + 3] * inv)};
+      *reinterpret_cast<u32x2_t*>(ost + l32 * C::ROWB + 16 * ((4 * db + g4) ^ (l32 & (C::CPR - 1))) + 8 * g) = v;
     }
-    if (g == 0) a.lse[qrow] = (m_run + fast_log2(lt)) * kLn2;
+  }
+  if (valid && g == 0) a.lse[qrow] = (m_run + fast_log2(lt)) * kLn2;
+  __syncthreads();
+  constexpr int NOUT = kWaveRows * C::CPR / 64;  // 16-byte stores per lane
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) {
+    const int p = 64 * k + lane;
+    const int row = p / C::CPR;
+    const int ch = p % C::CPR;
+    const int rr = wave * kWaveRows + row;
+    const int tk = rr / a.g;
+    const int hh = rr - tk * a.g;
+    const int tkn = it.q_begin + tk;
+    if (tk < a.tile_tokens && tkn < it.q_end) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ost + row * C::ROWB + 16 * (ch ^ (row & (C::CPR - 1))));
+      __bf16* op = reinterpret_cast<__bf16*>(a.o) + ((size_t)tkn * a.hq + h_kv * a.g + hh) * D + 8 * ch;
+      __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(op));
+    }
   }
 }
 
