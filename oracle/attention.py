@@ -20,9 +20,10 @@ K/V block is appended, stored K/V values are multiplied by the per-tensor
 k_scale / v_scale, and draft row t (position prefix_b + t) attends causally
 over that concatenation.
 
-Readings where the pages are silent are listed in the repository's design
-notes: prefix rows are queries too; causality includes the diagonal; GQA
-maps consecutive query heads to one kv head; LSE is a natural log.
+Where the pages are silent this oracle reads them as follows: prefix rows
+are queries too (they see the prefix causally); causality includes the
+diagonal; GQA maps consecutive query heads to one kv head; LSE is a natural
+log.  O and LSE are returned in float64.
 
 No blocking, fusion or reordering beyond row-chunking of the matmuls (to
 bound memory) is done here.

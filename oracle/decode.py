@@ -1,11 +1,11 @@
 """Exact decoding of stored element bytes to float64 (oracle, test-only).
 
 Storage codes: 0 = IEEE fp32, 1 = bfloat16 (upper half of an fp32),
-2 = OCP fp8 e4m3fn.  The fp8 variant is the one gfx950 implements natively
-(the verify page only says K/V may be fp8 with per-tensor scaling; reading
-recorded in the design doc): sign bit, 4 exponent bits with bias 7, 3 mantissa
-bits, no infinities, codes 0x7F / 0xFF are NaN, largest finite value 448,
-subnormals m/8 * 2^-6.
+2 = OCP fp8 e4m3fn.  The verify page only says that K/V may be fp8 with
+per-tensor scaling; the variant read here is the one gfx950 implements
+natively: sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+infinities, codes 0x7F / 0xFF are NaN, largest finite value 448, subnormals
+m/8 * 2^-6.
 
 Pinned by tests/test_oracle_decode.py against PyTorch's own dtype casts.
 """
