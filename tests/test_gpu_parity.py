@@ -53,6 +53,13 @@ def test_grpo_fullsize_sampled(gpu_lib):
     _flat_check(gpu_lib, inst, rows=_sample_rows(inst))
 
 
+@pytest.mark.parametrize("n", [1, 16])
+def test_grpo_rollout_count_sampled(gpu_lib, n):
+    # the read-once sweep's extremes: one rollout, and sixteen (T = 10240)
+    inst = make_flat(2048, [512] * n, 32, 8, 128, dtype=BF16, seed=200 + n, name=f"grpo_n{n}")
+    _flat_check(gpu_lib, inst, rows=_sample_rows(inst))
+
+
 def test_grpo_ragged_fullsize_sampled(gpu_lib):
     inst = make_config("grpo_ragged")
     _flat_check(gpu_lib, inst, rows=_sample_rows(inst, n_random=24))
