@@ -169,6 +169,43 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
                          void* stream);
 
 /*
+ * Backward of the flat forward (PrefixSharing PR #50, "关键变更" / key
+ * changes: the rollouts' KV is built by copying the prefix with .copy_(), so
+ * gradients flow back through the copies and a stored prefix row receives the
+ * sum of all its copies' gradients; equivalently, the gradient of one
+ * attention over the flat buffer with the block-causal visibility).  The
+ * flat output's prefix rows count once.
+ *
+ * Bytes of scratch psattn_bwd needs (flat mode only): lse2 and delta, [T, Hq]
+ * fp32 each, and fp32 dK / dV accumulators, [T, Hkv, D] each.  Host only.
+ * Returns 0 and sets the last error on invalid or unsupported input.
+ */
+size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                                 psattn_dtype dtype);
+
+/*
+ * Gradients dQ, dK, dV of the flat forward for the upstream gradient dO.
+ *   q, k, v, o   : the forward's inputs and output ([T, Hq, D], [T, Hkv, D],
+ *                  [T, Hkv, D], [T, Hq, D]); device, 16-byte aligned.
+ *   lse          : the forward's LSE [T, Hq], fp32, natural log.
+ *   dout         : dO [T, Hq, D], q's dtype.
+ *   dq, dk, dv   : outputs, layouts of q, k, v, in q's dtype; fully written.
+ *   desc         : flat descriptor (mode PSATTN_MODE_FLAT), as for psattn_fwd.
+ *   d            : 128.  dtype: PSATTN_BF16.  hq / hkv <= 64.
+ *   sm_scale     : the forward's logit scale.
+ *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,
+ *                  256-byte aligned; its contents on entry do not matter.
+ * Enqueues four launches on `stream` (row terms, dQ, dK/dV, conversion).
+ * dK and dV sum fp32 partials with atomic adds, so their last bits may
+ * differ between calls; dQ is deterministic.  Other configurations return
+ * PSATTN_E_UNSUPPORTED with nothing enqueued.
+ */
+psattn_status psattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, const psattn_desc* desc,
+                         int32_t hq, int32_t hkv, int32_t d, float sm_scale, psattn_dtype dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Test hook: run the segment planner ON THE DEVICE for every workgroup of the
  * prefix-pass launch psattn_fwd would make and write its work items
  * (PSATTN_ITEM_FIELDS int32 each, in workgroup order) to items_dev, which

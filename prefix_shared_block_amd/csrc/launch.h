@@ -49,6 +49,38 @@ struct PagedArgs {
   float v_scale;
 };
 
+// Backward of the flat forward (bf16).  Workspace: lse2 and delta [T, Hq]
+// fp32, acc_k and acc_v [T, Hkv, D] fp32.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;   // forward LSE, natural log, [T, Hq]
+  const void* dout;   // dO [T, Hq, D]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse2;   // LSE log2(e)
+  float* delta;  // sum_d dO O
+  float* acc_k;
+  float* acc_v;
+  const int32_t* seg_offsets;
+  int64_t total_tokens;
+  int32_t prefix_len;
+  int32_t nseg;
+  int32_t hq;
+  int32_t hkv;
+  int32_t g;
+  int32_t tile_tokens;  // query tokens per dQ item (the forward's)
+  int32_t row_chunk;    // query tokens per dK/dV item
+  float scale_log2;     // sm_scale * log2(e)
+  float sm_scale;
+};
+// pre (delta, lse2, zeroed accumulators), dQ, dK/dV and the final conversion,
+// defined in psattn_bwd.hip
+int launch_flat_bwd(const BwdArgs& a, int d, int64_t dq_blocks, int64_t dkdv_blocks, void* stream);
+
 // dtype codes follow psattn_dtype (0 f32, 1 bf16, 2 fp8 e4m3fn)
 int launch_flat(const FlatArgs& a, int d, int dtype, int64_t n_blocks, void* stream);
 // bf16 flat kernel, defined in psattn_flat.hip

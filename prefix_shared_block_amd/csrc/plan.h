@@ -247,6 +247,84 @@ PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, in
   return s;
 }
 
+// ------------------------------------------------- backward (flat) dK/dV plan
+// The key-major pass of the backward takes keys [k0, k1) of one kv head (at
+// most kBwdKeys, inside the prefix or inside one rollout) against the query
+// tokens [r0, r1) of one chunk (at most `rc` tokens) of a row range that sees
+// those keys.  Prefix keys are seen by the prefix rows from k0 on and by every
+// rollout's rows; a rollout's keys by that rollout's rows from k0 on.  Items
+// of one kv head, in order: the prefix key tiles, each with its prefix-row
+// chunks and then every rollout's chunks (rollouts in order); then every
+// rollout's key tiles in order, each with its own row chunks.
+constexpr int kBwdKeys = 128;
+
+struct BwdItem {
+  int32_t valid, k0, k1, r0, r1;
+};
+
+PS_HD BwdItem dkdv_item(int32_t j, int32_t prefix_len, int32_t nseg, const int32_t* seg_offsets, int32_t rc) {
+  BwdItem it{0, 0, 0, 0, 0};
+  int32_t rem = j;
+  int32_t sr = 0;  // chunks of all rollouts' rows
+  for (int32_t i = 0; i < nseg; ++i) sr += cdiv32(seg_offsets[i + 1] - seg_offsets[i], rc);
+  const int32_t npk = cdiv32(prefix_len, kBwdKeys);
+  for (int32_t t = 0; t < npk; ++t) {
+    const int32_t k0 = t * kBwdKeys;
+    const int32_t np = cdiv32(prefix_len - k0, rc);
+    if (rem < np + sr) {
+      it.k0 = k0;
+      it.k1 = imin(k0 + kBwdKeys, prefix_len);
+      if (rem < np) {
+        it.valid = 1;
+        it.r0 = k0 + rem * rc;
+        it.r1 = imin(it.r0 + rc, prefix_len);
+        return it;
+      }
+      rem -= np;
+      for (int32_t i = 0; i < nseg; ++i) {
+        const int32_t a = seg_offsets[i], b = seg_offsets[i + 1];
+        const int32_t ni = cdiv32(b - a, rc);
+        if (rem < ni) {
+          it.valid = 1;
+          it.r0 = a + rem * rc;
+          it.r1 = imin(it.r0 + rc, b);
+          return it;
+        }
+        rem -= ni;
+      }
+      it.k0 = it.k1 = 0;
+      return it;
+    }
+    rem -= np + sr;
+  }
+  for (int32_t i = 0; i < nseg; ++i) {
+    const int32_t a = seg_offsets[i], b = seg_offsets[i + 1];
+    for (int32_t k0 = a; k0 < b; k0 += kBwdKeys) {
+      const int32_t n = cdiv32(b - k0, rc);
+      if (rem < n) {
+        it.valid = 1;
+        it.k0 = k0;
+        it.k1 = imin(k0 + kBwdKeys, b);
+        it.r0 = k0 + rem * rc;
+        it.r1 = imin(it.r0 + rc, b);
+        return it;
+      }
+      rem -= n;
+    }
+  }
+  return it;
+}
+
+// Upper bound on the dK/dV items of one kv head from host scalars only.
+PS_HD int64_t dkdv_items_per_head_ub(int64_t prefix_len, int64_t total, int64_t nseg, int64_t max_seg,
+                                     int64_t rc) {
+  const int64_t suf = total - prefix_len;
+  const int64_t sr = cdiv64(suf, rc) + nseg;  // >= sum_i ceil(S_i / rc)
+  const int64_t pre = cdiv64(prefix_len, kBwdKeys) * (cdiv64(prefix_len, rc) + sr);
+  const int64_t rtiles = suf / kBwdKeys + nseg;  // >= number of rollout key tiles
+  return pre + rtiles * cdiv64(max_seg, rc);
+}
+
 // ---------------------------------------------------------------- flat plan
 PS_HD int64_t flat_items_per_head_ub(int64_t prefix_len, int64_t total, int64_t nseg, int64_t tt) {
   return cdiv64(prefix_len, tt) + (total - prefix_len) / tt + nseg;

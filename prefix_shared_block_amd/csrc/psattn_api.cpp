@@ -118,6 +118,39 @@ psattn_status check_common(const psattn_desc* d, int32_t hq, int32_t hkv, int32_
   return PSATTN_OK;
 }
 
+// ---------------------------------------------------------------- backward
+constexpr int32_t kBwdRowChunk = 512;  // query tokens per dK/dV item
+
+struct BwdPlan {
+  Plan base;
+  int64_t dq_blocks = 0;
+  int64_t dkdv_blocks = 0;
+  size_t off_delta = 0, off_acck = 0, off_accv = 0, ws_bytes = 0;
+};
+
+psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t hd, psattn_dtype dt,
+                        BwdPlan* bp) {
+  if (d && d->mode != PSATTN_MODE_FLAT) return fail(PSATTN_E_UNSUPPORTED, "the backward covers the flat layout only");
+  psattn_status st = check_common(d, hq, hkv, hd, dt, dt, &bp->base);
+  if (st != PSATTN_OK) return st;
+  if (dt != PSATTN_BF16) return fail(PSATTN_E_UNSUPPORTED, "the backward takes bf16 only");
+  if (hd != 128) return fail(PSATTN_E_UNSUPPORTED, "the backward takes head dim 128 only (got %d)", hd);
+  if (bp->base.g > 64) return fail(PSATTN_E_UNSUPPORTED, "the backward takes GQA groups up to 64 (got %d)", bp->base.g);
+  const int64_t t = d->total_tokens;
+  bp->dq_blocks = bp->base.flat_blocks;
+  bp->dkdv_blocks =
+      t == 0 ? 0
+             : dkdv_items_per_head_ub(d->prefix_len, t, d->num_segments, d->max_seg_len, kBwdRowChunk) * hkv;
+  if (bp->dkdv_blocks > INT32_MAX) return fail(PSATTN_E_UNSUPPORTED, "grid too large");
+  const size_t rows = (size_t)t * hq * sizeof(float);
+  const size_t acc = (size_t)t * hkv * hd * sizeof(float);
+  bp->off_delta = round_up(rows, kWsAlign);
+  bp->off_acck = bp->off_delta + round_up(rows, kWsAlign);
+  bp->off_accv = bp->off_acck + round_up(acc, kWsAlign);
+  bp->ws_bytes = t == 0 ? 0 : bp->off_accv + round_up(acc, kWsAlign);
+  return PSATTN_OK;
+}
+
 void fill_info(const Plan& p, psattn_plan_info* info) {
   if (!info) return;
   std::memset(info, 0, sizeof(*info));
@@ -231,6 +264,65 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
     a.v_scale = v_scale;
     err = launch_paged(a, d, (int)q_dtype, (int)kv_dtype, p.pg, p.paged_blocks, stream);
   }
+  if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
+  return PSATTN_OK;
+}
+
+size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                                 psattn_dtype dtype) {
+  g_last_error.clear();
+  BwdPlan bp;
+  if (check_bwd(desc, hq, hkv, d, dtype, &bp) != PSATTN_OK) return 0;
+  return bp.ws_bytes;
+}
+
+psattn_status psattn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, const psattn_desc* desc,
+                         int32_t hq, int32_t hkv, int32_t d, float sm_scale, psattn_dtype dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  BwdPlan bp;
+  psattn_status st = check_bwd(desc, hq, hkv, d, dtype, &bp);
+  if (st != PSATTN_OK) return st;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(PSATTN_E_INVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (desc->total_tokens == 0) return PSATTN_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(PSATTN_E_INVAL, "q, k, v, o, lse, dout, dq, dk and dv must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+    return fail(PSATTN_E_INVAL, "tensors must be 16-byte aligned and lse 4-byte aligned");
+  if (!workspace || workspace_bytes < bp.ws_bytes)
+    return fail(PSATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", bp.ws_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, kWsAlign)) return fail(PSATTN_E_INVAL, "workspace must be 256-byte aligned");
+  char* ws = reinterpret_cast<char*>(workspace);
+  BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.lse2 = reinterpret_cast<float*>(ws);
+  a.delta = reinterpret_cast<float*>(ws + bp.off_delta);
+  a.acc_k = reinterpret_cast<float*>(ws + bp.off_acck);
+  a.acc_v = reinterpret_cast<float*>(ws + bp.off_accv);
+  a.seg_offsets = desc->seg_offsets;
+  a.total_tokens = desc->total_tokens;
+  a.prefix_len = desc->prefix_len;
+  a.nseg = desc->num_segments;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.g = bp.base.g;
+  a.tile_tokens = bp.base.fg.tile_tokens;
+  a.row_chunk = kBwdRowChunk;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.sm_scale = sm_scale;
+  const int err = launch_flat_bwd(a, d, bp.dq_blocks, bp.dkdv_blocks, stream);
   if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
   return PSATTN_OK;
 }

@@ -88,6 +88,10 @@ def load(path: Optional[str] = None):
     lib.psattn_plan_dump.restype = i32
     lib.psattn_plan_host.argtypes = [dp, i32, i32, i32, i32, i32, vp, i64, ip]
     lib.psattn_plan_host.restype = i32
+    lib.psattn_bwd_workspace_size.argtypes = [dp, i32, i32, i32, i32]
+    lib.psattn_bwd_workspace_size.restype = sz
+    lib.psattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dp, i32, i32, i32, f32, i32, vp, sz, vp]
+    lib.psattn_bwd.restype = i32
     lib.psattn_status_string.argtypes = [i32]
     lib.psattn_status_string.restype = ctypes.c_char_p
     lib.psattn_last_error.argtypes = []
@@ -118,6 +122,17 @@ def psattn_fwd(q: int, k: int, v: int, o: int, lse: int, desc: PsattnDesc, hq: i
                workspace: int, workspace_bytes: int, stream: int) -> int:
     return int(load().psattn_fwd(q, k, v, o, lse, _ref(desc), hq, hkv, d, sm_scale, q_dtype,
                                  kv_dtype, k_scale, v_scale, workspace, workspace_bytes, stream))
+
+
+def psattn_bwd_workspace_size(desc: PsattnDesc, hq: int, hkv: int, d: int, dtype: int) -> int:
+    return int(load().psattn_bwd_workspace_size(_ref(desc), hq, hkv, d, dtype))
+
+
+def psattn_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+               desc: PsattnDesc, hq: int, hkv: int, d: int, sm_scale: float, dtype: int, workspace: int,
+               workspace_bytes: int, stream: int) -> int:
+    return int(load().psattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, _ref(desc), hq, hkv, d, sm_scale, dtype,
+                                 workspace, workspace_bytes, stream))
 
 
 def psattn_plan_dump(desc: PsattnDesc, hq: int, hkv: int, d: int, q_dtype: int, kv_dtype: int,
@@ -215,6 +230,35 @@ def fwd_flat(q, k, v, prefix_len: int, seg_offsets, max_seg_len: int, sm_scale: 
                     qdt, _dtype_code(k), 1.0, 1.0, 0, 0, _stream_handle(q.device))
     check(st)
     return out, lse
+
+
+def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: int,
+             sm_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of the flat forward for the upstream gradient dout.  o and
+    lse are the forward's outputs; shapes and the descriptor as in fwd_flat.
+    Returns (dq, dk, dv)."""
+    import torch
+
+    t_n, hq, d = q.shape
+    hkv = k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    n = int(seg_offsets.numel()) - 1 if seg_offsets is not None else 0
+    desc = flat_desc(t_n, prefix_len, n, _ptr(seg_offsets), max_seg_len)
+    dt = _dtype_code(q)
+    ws_bytes = psattn_bwd_workspace_size(desc, hq, hkv, d, dt)
+    if ws_bytes == 0 and t_n > 0:
+        raise PsattnError(2, psattn_last_error())
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    wsz = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = psattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), desc,
+                    hq, hkv, d, float(sm_scale), dt, _ptr(workspace), wsz, _stream_handle(q.device))
+    check(st)
+    return dq, dk, dv
 
 
 def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext, draft_len: int,

@@ -224,3 +224,46 @@ def test_paged_planner_matches_enumeration(lib, prefix_lens, lx, hq, hkv, d, kvd
     assert info.n_splits * info.split_len >= pl.max()
     ref = enumerate_paged(pl, hkv, lx, info.n_splits, info.split_len)
     assert np.array_equal(items, ref)
+
+
+# ------------------------------------------------------------------ backward
+def _bwd(desc, hq=8, hkv=2, d=128, dt=ps.BF16, sm=0.088, ptr=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40):
+    return ps.psattn_bwd(ptr, ptr, ptr, ptr, lse, ptr, ptr, ptr, ptr, desc, hq, hkv, d, sm, dt, ws, wsb, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=64), ps.E_UNSUPPORTED),
+    (dict(d=256), ps.E_UNSUPPORTED),
+    (dict(dt=ps.F32), ps.E_UNSUPPORTED),
+    (dict(dt=ps.FP8), ps.E_UNSUPPORTED),
+    (dict(hq=128, hkv=1), ps.E_UNSUPPORTED),   # G = 128 > 64
+    (dict(hq=7, hkv=2), ps.E_INVAL),
+    (dict(sm=-1.0), ps.E_INVAL),
+    (dict(ptr=0), ps.E_INVAL),
+    (dict(ptr=FAKE + 4), ps.E_INVAL),
+    (dict(lse=FAKE + 1), ps.E_INVAL),
+    (dict(ws=0), ps.E_WORKSPACE),
+    (dict(wsb=1024), ps.E_WORKSPACE),
+    (dict(ws=FAKE + 16), ps.E_INVAL),          # workspace not 256-byte aligned
+])
+def test_bwd_validation(lib, kw, status):
+    assert _bwd(_flat(t=96, p=64, n=2, mx=16), **kw) == status
+    assert ps.psattn_last_error()
+
+
+def test_bwd_paged_mode_unsupported(lib):
+    assert _bwd(_paged()) == ps.E_UNSUPPORTED
+    assert ps.psattn_bwd_workspace_size(_paged(), 8, 2, 128, ps.BF16) == 0
+
+
+def test_bwd_workspace_size(lib):
+    # lse2 and delta [T, Hq] fp32, then the dK / dV accumulators [T, Hkv, D] fp32, each 256-byte aligned
+    t, hq, hkv, d = 96, 8, 2, 128
+    up = lambda x: (x + 255) // 256 * 256
+    want = 2 * up(t * hq * 4) + 2 * up(t * hkv * d * 4)
+    assert ps.psattn_bwd_workspace_size(_flat(t=t, p=64, n=2, mx=16), hq, hkv, d, ps.BF16) == want
+    assert ps.psattn_bwd_workspace_size(ps.flat_desc(0, 0, 0, 0, 0), hq, hkv, d, ps.BF16) == 0
+
+
+def test_bwd_empty_enqueues_nothing(lib):
+    assert _bwd(ps.flat_desc(0, 0, 0, 0, 0), ptr=0, lse=0, ws=0, wsb=0) == ps.OK
