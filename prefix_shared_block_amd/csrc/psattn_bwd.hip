@@ -138,15 +138,15 @@ void bwd_dq_kernel(BwdArgs a) {
   const char* wbase = w_isv ? vbase : kbase;
   // K is read by rows and transposed (swizzle fb), V by rows only (fk)
   auto swz = [&](int row) __attribute__((always_inline)) { return w_isv ? C::fk(row) : C::fb(row); };
-  uint32_t coff[CPW];
-#pragma unroll
-  for (int t = 0; t < CPW; ++t) {
-    const int jb = (wave * CPW + t) % NCOPY;
-    const int p = jb * 64 + lane;
-    const int row = p / C::CPR;
-    const int pos = p % C::CPR;
-    coff[t] = (uint32_t)row * row_stride + 16u * (uint32_t)(pos ^ swz(row));
-  }
+  // Copy t of this wave is 1 KiB block jb = (wave CPW + t) mod NCOPY: rows
+  // 4 jb .. 4 jb + 3 (the row part of the source offset goes to the scalar
+  // base), lane l on row 4 jb + l / 16, chunk l % 16.  With 16 chunks per row
+  // both swizzles reduce to copy 0's lane offset with bits flipped by t & 3:
+  // bits 4..5 for fb (K), bits 6..7 for fk (V).
+  static_assert(C::CPR == 16 && CPW % 4 == 0, "copy offsets repeat with period 4");
+  const uint32_t coff0 = (uint32_t)(lane / C::CPR) * row_stride +
+                         16u * (uint32_t)((lane % C::CPR) ^ swz(4 * ((wave * CPW) % NCOPY) + lane / C::CPR));
+  const uint32_t cflip = w_isv ? 64u : 16u;
   auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
     const uint32_t bofs = (uint32_t)bsel * (2 * TILE);
     int k0, ke;
@@ -156,7 +156,8 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < CPW; ++t) {
         const int jb = (wave * CPW + t) % NCOPY;
-        dma16_s(base, coff[t], lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
+        dma16_s(base + (size_t)(4 * jb) * row_stride, coff0 ^ (cflip * (uint32_t)(t & 3)),
+                lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
       }
     } else {
       const int lastr = ke - 1 - k0;
@@ -187,40 +188,38 @@ void bwd_dq_kernel(BwdArgs a) {
   auto math = [&](const char* kt, const char* vt, int key0, int kend, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
     // lane (l32, g), reg i of block kb: key 32 kb + 8 (i / 4) + 4 g + i % 4 of row l32
-    f32x16_t sc[2], dp[2];
+    int lim = BN;
+    if constexpr (MASK) lim = (kend < token + 1 ? kend : token + 1) - key0;
+    bf16x8_t dst[4];  // k-step ks = 2 kb + half: regs 8 half .. 8 half + 7 of block kb
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16_t sc, dp;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sc[kb][e] = 0.f;
-        dp[kb][e] = 0.f;
+        sc[e] = 0.f;
+        dp[e] = 0.f;
       }
       const int row = 32 * kb + l32;
 #pragma unroll
       for (int s = 0; s < C::NSTEP; ++s) {
         const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kb], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc, 0, 0, 0);
       }
 #pragma unroll
       for (int s = 0; s < C::NSTEP; ++s) {
         const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fk(row)));
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[s], dp[kb], 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[s], dp, 0, 0, 0);
       }
-    }
-    int lim = BN;
-    if constexpr (MASK) lim = (kend < token + 1 ? kend : token + 1) - key0;
-    bf16x8_t dst[4];  // k-step ks = 2 kb + half: regs 8 half .. 8 half + 7 of block kb
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -lse2));
+        float p = fast_exp2(__builtin_fmaf(sc[i], c, -lse2));
         if constexpr (MASK) {
           const int kr = 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
           p = kr < lim ? p : 0.f;
         }
-        dst[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dp[kb][i] - delta));
+        dst[2 * kb + (i >> 3)][i & 7] = (__bf16)(p * (dp[i] - delta));
       }
+    }
     // dQ^T += K^T dS^T: A operand lane (d, g) = K rows 16 ks + 8 t + 4 g + 0..3
     // of column d, read transposed
 #pragma unroll
@@ -302,7 +301,10 @@ void bwd_dq_kernel(BwdArgs a) {
 
 // --------------------------------------------------------------- dK/dV pass
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// One wave per SIMD: the fixed K^T / V^T fragments (64 VGPRs) and the two
+// accumulators (128) leave too little of a 256-register budget; at two waves
+// per SIMD the spills cost more than the second wave gains.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int RT = 64;                  // stacked query rows per tile
