@@ -40,25 +40,32 @@ _ROW_CHUNK = 512
 
 
 def causal_attention_bwd(qx: np.ndarray, kx: np.ndarray, vx: np.ndarray, dox: np.ndarray,
-                         sm_scale: float):
+                         sm_scale: float, q_rows=None, k_rows=None):
     """Backward of causal softmax attention over one whole sequence.
 
     qx, dox: [L, Hq, D] float64 queries and upstream output gradient;
     kx, vx:  [L, Hkv, D] float64 keys and values.  Row r sees keys j <= r.
-    Returns dQ [L, Hq, D], dK [L, Hkv, D], dV [L, Hkv, D] (float64).
+    q_rows / k_rows: optional index arrays restricting which dQ rows and which
+    dK / dV rows are returned (every row's softmax terms are still formed).
+    Returns dQ [L or |q_rows|, Hq, D], dK and dV [L or |k_rows|, Hkv, D].
     """
     l_n, hq, d = qx.shape
     hkv = kx.shape[1]
     if hq % hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     g = hq // hkv
-    dq = np.zeros((l_n, hq, d), dtype=np.float64)
-    dk = np.zeros((l_n, hkv, d), dtype=np.float64)
-    dv = np.zeros((l_n, hkv, d), dtype=np.float64)
+    qsel = np.arange(l_n) if q_rows is None else np.asarray(q_rows, dtype=np.int64)
+    ksel = np.arange(l_n) if k_rows is None else np.asarray(k_rows, dtype=np.int64)
+    qpos = np.full(l_n, -1, dtype=np.int64)
+    qpos[qsel] = np.arange(qsel.size)
+    dq = np.zeros((qsel.size, hq, d), dtype=np.float64)
+    dk = np.zeros((ksel.size, hkv, d), dtype=np.float64)
+    dv = np.zeros((ksel.size, hkv, d), dtype=np.float64)
     cols = np.arange(l_n)
     for c0 in range(0, l_n, _ROW_CHUNK):
         c1 = min(l_n, c0 + _ROW_CHUNK)
         masked = cols[None, :] > np.arange(c0, c1)[:, None]
+        want = qpos[c0:c1] >= 0
         for h in range(hq):
             kvh = h // g
             z = (qx[c0:c1, h, :] @ kx[:, kvh, :].T) * sm_scale
@@ -67,23 +74,25 @@ def causal_attention_bwd(qx: np.ndarray, kx: np.ndarray, vx: np.ndarray, dox: np
             p = np.exp(z - m[:, None])
             p /= p.sum(axis=1)[:, None]
             do_r = dox[c0:c1, h, :]
-            dv[:, kvh, :] += p.T @ do_r
             dp = do_r @ vx[:, kvh, :].T
             delta = (p * dp).sum(axis=1)
             ds = p * (dp - delta[:, None])
-            dq[c0:c1, h, :] = (ds @ kx[:, kvh, :]) * sm_scale
-            dk[:, kvh, :] += (ds.T @ qx[c0:c1, h, :]) * sm_scale
+            dv[:, kvh, :] += p[:, ksel].T @ do_r
+            dk[:, kvh, :] += (ds[:, ksel].T @ qx[c0:c1, h, :]) * sm_scale
+            if want.any():
+                dq[qpos[c0:c1][want], h, :] = (ds[want] @ kx[:, kvh, :]) * sm_scale
     return dq, dk, dv
 
 
 def attn_flat_bwd(q, k, v, do, prefix_len: int, seg_offsets: Sequence[int], sm_scale: float,
-                  dtype: int = 0):
+                  dtype: int = 0, rows=None, keys=None):
     """Gradients of the flat-packed forward [P | S1 | ... | SN].
 
     q, do: [T, Hq, D]; k, v: [T, Hkv, D], in storage form ``dtype`` (0 fp32,
     1 bf16 bits) or already float64 when dtype is None.  seg_offsets: N+1
-    offsets, seg_offsets[0] = P, seg_offsets[N] = T.
-    Returns dQ [T, Hq, D], dK [T, Hkv, D], dV [T, Hkv, D] in float64.
+    offsets, seg_offsets[0] = P, seg_offsets[N] = T.  rows / keys: optional
+    flat indices restricting which dQ rows and which dK / dV rows are formed.
+    Returns dQ [T or |rows|, Hq, D], dK and dV [T or |keys|, Hkv, D] in float64.
     """
     def dec(x):
         return x if dtype is None else decode(x, dtype)
@@ -95,9 +104,15 @@ def attn_flat_bwd(q, k, v, do, prefix_len: int, seg_offsets: Sequence[int], sm_s
     n = len(offs) - 1
     if offs[0] != p or offs[-1] != t_n or any(b < a for a, b in zip(offs, offs[1:])):
         raise ValueError("bad seg_offsets")
-    dq = np.zeros((t_n, hq, d), dtype=np.float64)
-    dk = np.zeros((t_n, hkv, d), dtype=np.float64)
-    dv = np.zeros((t_n, hkv, d), dtype=np.float64)
+    want_r = np.arange(t_n) if rows is None else np.asarray(rows, dtype=np.int64)
+    want_k = np.arange(t_n) if keys is None else np.asarray(keys, dtype=np.int64)
+    slot_r = np.full(t_n, -1, dtype=np.int64)
+    slot_r[want_r] = np.arange(want_r.size)
+    slot_k = np.full(t_n, -1, dtype=np.int64)
+    slot_k[want_k] = np.arange(want_k.size)
+    dq = np.zeros((want_r.size, hq, d), dtype=np.float64)
+    dk = np.zeros((want_k.size, hkv, d), dtype=np.float64)
+    dv = np.zeros((want_k.size, hkv, d), dtype=np.float64)
     segs = [(offs[i], offs[i + 1]) for i in range(n)] if n > 0 else [(p, p)]
     for si, (a, b) in enumerate(segs):
         idx = np.concatenate([np.arange(p), np.arange(a, b)]).astype(np.int64)
@@ -109,9 +124,11 @@ def attn_flat_bwd(q, k, v, do, prefix_len: int, seg_offsets: Sequence[int], sm_s
         dox = np.array(dec(build_kv(do, p, a, b)), dtype=np.float64)
         if si > 0:
             dox[:p] = 0.0  # the flat prefix rows are expansion 0's
-        gq, gk, gv = causal_attention_bwd(qx, kx, vx, dox, sm_scale)
-        # idx holds distinct stored rows, so each copy adds once
-        dq[idx] += gq
-        dk[idx] += gk
-        dv[idx] += gv
+        lr = np.nonzero(slot_r[idx] >= 0)[0]  # local rows / keys of this expansion that are wanted
+        lk = np.nonzero(slot_k[idx] >= 0)[0]
+        gq, gk, gv = causal_attention_bwd(qx, kx, vx, dox, sm_scale, q_rows=lr, k_rows=lk)
+        # each stored row appears once per expansion, so each copy adds once
+        dq[slot_r[idx[lr]]] += gq
+        dk[slot_k[idx[lk]]] += gk
+        dv[slot_k[idx[lk]]] += gv
     return dq, dk, dv

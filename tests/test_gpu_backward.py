@@ -101,6 +101,33 @@ def test_bwd_grpo_block(gpu_lib):
     _check(gpu_lib, inst)
 
 
+def test_bwd_grpo_fullsize_sampled(gpu_lib):
+    # the full GRPO shape in the benchmark's launch configuration; dQ rows and
+    # dK / dV rows sampled at the prefix and rollout boundaries, at tile edges
+    # and at seeded random positions
+    from psattn_inputs import make_config
+
+    inst = make_config("grpo")
+    do_bits = _dout(inst, 7)
+    (dq, dk, dv), = _run(gpu_lib, inst, do_bits)
+    t, p = inst.total_tokens, inst.prefix_len
+    rng = np.random.default_rng(9)
+    edges = [0, 1, 63, 64, 127, 128, p - 1, p, p + 1, p + 511, p + 512, t - 1]
+    rows = np.unique(np.concatenate([edges, rng.choice(t, 8, replace=False)]))
+    keys = np.unique(np.concatenate([edges, rng.choice(t, 6, replace=False)]))
+    ref = attn_flat_bwd(inst.q, inst.k, inst.v, do_bits, p, inst.seg_offsets, inst.sm_scale, dtype=BF16,
+                        rows=rows, keys=keys)
+    got = (to_f64(dq)[rows], to_f64(dk)[keys], to_f64(dv)[keys])
+    top_max = max(np.max(np.abs(r)) for r in ref)
+    top_mean = max(np.mean(np.abs(r)) for r in ref)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        assert np.all(np.isfinite(g)), name
+        dmax = np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-2 * top_max)
+        dmean = np.mean(np.abs(g - r)) / max(np.mean(np.abs(r)), 1e-2 * top_mean)
+        print(f"[bwd parity] grpo sampled {name}: max {dmax:.2e} mean {dmean:.2e}", flush=True)
+        assert dmax <= TOL_MAX_REL and dmean <= TOL_MEAN_REL, (name, dmax, dmean)
+
+
 def test_bwd_workspace_contents_do_not_matter_and_dq_is_deterministic(gpu_lib):
     inst = make_flat(200, [90, 140, 33], 16, 4, 128, dtype=BF16, seed=43)
     do_bits = _dout(inst, 3)

@@ -162,3 +162,15 @@ def test_backward_reads_bf16_storage():
                         dtype=BF16)
     for a, b in zip(got, want):
         assert np.array_equal(a, b)
+
+
+def test_backward_restricted_rows_and_keys_match_the_full_result():
+    p, lens, hq, hkv, d = 7, [6, 3, 9], 8, 2, 4
+    q, k, v, do, offs = _rand(17, p, lens, hq, hkv, d)
+    full = attn_flat_bwd(q, k, v, do, p, offs, 0.6, dtype=None)
+    rows = np.array([0, 3, 6, 7, 12, 20, 24])
+    keys = np.array([1, 5, 6, 8, 14, 15, 24])
+    dq, dk, dv = attn_flat_bwd(q, k, v, do, p, offs, 0.6, dtype=None, rows=rows, keys=keys)
+    assert np.allclose(dq, full[0][rows], rtol=0, atol=1e-13)
+    assert np.allclose(dk, full[1][keys], rtol=0, atol=1e-13)
+    assert np.allclose(dv, full[2][keys], rtol=0, atol=1e-13)
