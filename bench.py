@@ -115,6 +115,41 @@ class FlatRunner:
         return compare(to_f64(self.o)[rows], to_f64(self.lse)[rows], ro, rl, "bf16", inst.name)
 
 
+class BwdRunner:
+    """The flat backward at one instance: forward outputs computed once, then
+    each call runs psattn_bwd (row terms, dQ, dK/dV, conversion)."""
+
+    def __init__(self, ps, inst):
+        import torch
+        from gpu_util import to_dev
+        from psattn_inputs import f32_to_bf16_bits
+
+        self.ps, self.inst = ps, inst
+        self.q = to_dev(inst.q, inst.dtype)
+        self.k = to_dev(inst.k, inst.dtype)
+        self.v = to_dev(inst.v, inst.dtype)
+        self.seg = torch.from_numpy(inst.seg_offsets).cuda()
+        self.o, self.lse = ps.fwd_flat(self.q, self.k, self.v, inst.prefix_len, self.seg, inst.max_seg_len,
+                                       sm_scale=inst.sm_scale)
+        rng = np.random.default_rng(inst.seed + 1000)
+        self.do = to_dev(f32_to_bf16_bits(rng.standard_normal(inst.q.shape).astype(np.float32)), inst.dtype)
+        self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
+        desc = ps.flat_desc(inst.total_tokens, inst.prefix_len, inst.num_segments, self.seg.data_ptr(),
+                            inst.max_seg_len)
+        nb = ps.psattn_bwd_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.dtype)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+
+    def __call__(self):
+        i = self.inst
+        self.ps.bwd_flat(self.q, self.k, self.v, self.o, self.lse, self.do, i.prefix_len, self.seg, i.max_seg_len,
+                         sm_scale=i.sm_scale, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+    def finite(self) -> bool:
+        import torch
+
+        return all(bool(torch.isfinite(t.float()).all().item()) for t in (self.dq, self.dk, self.dv))
+
+
 class PagedRunner:
     def __init__(self, ps, inst):
         import torch
@@ -240,7 +275,7 @@ def traffic_from_profile(kernel_prefix: str, grid: int):
     return None
 
 
-def prefix_sweep(ps, flush, calls: int, copy_calib: bool):
+def prefix_sweep(ps, flush, calls: int, copy_calib: bool, json_out=None):
     """The GRPO shape with N = 1, 2, 4, 8, 16 rollouts of 512 tokens (P = 2048,
     Hq = 32, Hkv = 8, D = 128, bf16): a few evicted calls each, for a counter
     run that checks that the prefix K/V is read about once per call whatever
@@ -269,7 +304,7 @@ def prefix_sweep(ps, flush, calls: int, copy_calib: bool):
             dst.copy_(src)
         torch.cuda.synchronize()
         out["copy_calib_bytes"] = {"read": n * 4, "write": n * 4}
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out), file=json_out or sys.stdout, flush=True)
 
 
 def main():
@@ -285,6 +320,10 @@ def main():
     ap.add_argument("--prefix-sweep", action="store_true",
                     help="instead of the benchmark: GRPO with 1..16 rollouts, for the prefix-K/V-read-once counter check")
     args = ap.parse_args()
+    # the one JSON line is the only thing on stdout; progress and parity
+    # reports go to stderr
+    json_out = sys.stdout
+    sys.stdout = sys.stderr
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -298,7 +337,7 @@ def main():
     torch.cuda.set_device(0)
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     if args.prefix_sweep:
-        prefix_sweep(ps, flush, max(1, args.steps), args.copy_calib)
+        prefix_sweep(ps, flush, max(1, args.steps), args.copy_calib, json_out)
         return
 
     log("generating grpo workload")
@@ -336,6 +375,17 @@ def main():
         "grpo_hbm_gbs": round(flat_alg_bytes(g_inst) / (tg["mean"] * 1e-3) / 1e9, 1),
     }
     del grpo
+
+    log("timing the grpo backward")
+    gb = BwdRunner(ps, g_inst)
+    tb = time_calls(gb, flush, max(3, args.steps // 3), 2)
+    assert gb.finite(), "non-finite gradients"
+    b_flops = 2.5 * g_flops  # S, dP, dV, dK and dQ products: 10 D flop per visible pair and query head
+    out["grpo_bwd"] = {"us": round(tb["mean"] * 1e3, 1), "us_min": round(tb["min"] * 1e3, 1),
+                       "useful_tflops": round(b_flops / (tb["mean"] * 1e-3) / 1e12, 2),
+                       "frac_mfma": round(b_flops / (tb["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "per_call_useful_flop": b_flops}
+    del gb
 
     log("generating verify16k workload")
     v_inst = make_config("verify16k")
@@ -390,7 +440,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu baseline)")
         out["cpu_baseline"] = cpu_baseline(g_inst, flat_useful_flops)
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out), file=json_out, flush=True)
 
 
 if __name__ == "__main__":
