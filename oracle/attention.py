@@ -75,6 +75,34 @@ def causal_attention(qr: np.ndarray, qpos: np.ndarray, kx: np.ndarray, vx: np.nd
     return o, lse
 
 
+def masked_attention(qr: np.ndarray, vis: np.ndarray, kx: np.ndarray, vx: np.ndarray, sm_scale: float):
+    """Softmax attention of query rows over the keys each of them sees.
+
+    qr:   [R, Hq, D] float64 query rows
+    vis:  [R, L] bool, row r sees key j iff vis[r, j]
+    kx,vx:[L, Hkv, D] float64 keys / values
+    Returns O [R, Hq, D] and LSE [R, Hq] (float64).
+    """
+    r_n, hq, d = qr.shape
+    hkv = kx.shape[1]
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = hq // hkv
+    o = np.empty((r_n, hq, d), dtype=np.float64)
+    lse = np.empty((r_n, hq), dtype=np.float64)
+    hidden = ~np.asarray(vis, dtype=bool)
+    for h in range(hq):
+        kvh = h // g
+        z = (qr[:, h, :] @ kx[:, kvh, :].T) * sm_scale
+        z[hidden] = -np.inf
+        m = z.max(axis=1)
+        p = np.exp(z - m[:, None])
+        s = p.sum(axis=1)
+        o[:, h, :] = (p @ vx[:, kvh, :]) / s[:, None]
+        lse[:, h] = m + np.log(s)
+    return o, lse
+
+
 def build_kv(x: np.ndarray, prefix_len: int, seg_begin: int, seg_end: int) -> np.ndarray:
     """Physical expansion of one rollout: a copy of [prefix | own segment]."""
     idx = np.concatenate([np.arange(prefix_len), np.arange(seg_begin, seg_end)])
@@ -152,12 +180,18 @@ def gather_prefix(pool: np.ndarray, kv_indptr, kv_indices, prefix_len: int, b: i
 def attn_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext,
                draft_len: int, sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
                q_dtype: int = 1, kv_dtype: int = 1, page_size: int = 16,
-               requests: Optional[Sequence[int]] = None):
+               requests: Optional[Sequence[int]] = None, draft_mask: Optional[np.ndarray] = None):
     """Reference for speculative verify over a paged prefix.
 
     q: [B*Lx, Hq, D]; k_pool/v_pool: [num_pages, page_size, Hkv, D];
     k_ext/v_ext: [B*Lx, Hkv, D] draft K/V.  Returns O [B*Lx, Hq, D], LSE [B*Lx, Hq]
     (rows of requests not listed in ``requests`` are NaN).
+
+    draft_mask: optional [B, Lx, Lx]; draft row t of request b sees draft key j
+    iff draft_mask[b, t, j] is nonzero (a draft tree: a token sees its
+    ancestors and itself), and every prefix key as before.  The sglang page's
+    verify takes such a custom mask over the draft part only (its prefix part is
+    skipped); without it, row t sees draft keys 0..t.
     """
     qf = decode(q, q_dtype)
     lx = int(draft_len)
@@ -174,8 +208,12 @@ def attn_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_e
         vd = decode(v_ext[b * lx:(b + 1) * lx], kv_dtype)
         kx = np.concatenate([kp, kd], axis=0) * k_scale
         vx = np.concatenate([vp, vd], axis=0) * v_scale
-        pos = pl + np.arange(lx)
-        oo, ll = causal_attention(qf[b * lx:(b + 1) * lx], pos, kx, vx, sm_scale)
+        if draft_mask is None:
+            pos = pl + np.arange(lx)
+            oo, ll = causal_attention(qf[b * lx:(b + 1) * lx], pos, kx, vx, sm_scale)
+        else:
+            vis = np.concatenate([np.ones((lx, pl), dtype=bool), np.asarray(draft_mask[b]) != 0], axis=1)
+            oo, ll = masked_attention(qf[b * lx:(b + 1) * lx], vis, kx, vx, sm_scale)
         o[b * lx:(b + 1) * lx] = oo
         lse[b * lx:(b + 1) * lx] = ll
     return o, lse

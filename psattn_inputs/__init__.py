@@ -302,6 +302,23 @@ def make_paged_spikes(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: 
 CONFIG_NAMES = ["tiny", "grpo", "verify16k", "verify_fp8", "grpo_ragged"]
 
 
+def make_tree_mask(batch: int, draft_len: int, seed: int, chain: bool = False) -> np.ndarray:
+    """Seeded draft trees as a [batch, draft_len, draft_len] uint8 visibility
+    mask: token t has a parent drawn uniformly from the earlier tokens (or none,
+    hanging off the prefix), and sees its ancestors and itself.  chain=True
+    gives the causal chain (the lower triangle)."""
+    rng = _rng(seed)
+    m = np.zeros((batch, draft_len, draft_len), dtype=np.uint8)
+    for b in range(batch):
+        parent = [-1] + [int(rng.integers(-1, t)) if not chain else t - 1 for t in range(1, draft_len)]
+        for t in range(draft_len):
+            j = t
+            while j >= 0:
+                m[b, t, j] = 1
+                j = parent[j]
+    return m
+
+
 def make_config(name: str, seed: Optional[int] = None):
     if name == "tiny":
         return make_flat(64, [16, 16], 2, 2, 64, dtype=F32, seed=1 if seed is None else seed,
