@@ -88,7 +88,15 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *   prefix_lens (device, int32, batch): 0 <= prefix_lens[b] <= max_prefix_len.
  *   max_prefix_len (host): upper bound of prefix_lens (sizes the split grid).
  *   k_ext, v_ext [batch * draft_len, Hkv, D] in kv dtype: the draft block's own
- *             K/V; draft row t sees draft keys 0..t.
+ *             K/V; draft row t sees draft keys 0..t, or, with draft_mask,
+ *             the draft keys its mask row marks.
+ *   draft_mask (device, uint8, [batch, draft_len, draft_len]) or NULL: a draft
+ *             tree (EAGLE top-k > 1; the sglang verify page's custom mask over
+ *             the draft part, prefix part skipped): draft row t of request b
+ *             sees draft key j iff draft_mask[(b * draft_len + t) * draft_len
+ *             + j] != 0, and every prefix key.  Each row must see itself (a
+ *             tree row holds its ancestors and its own token).  NULL: the
+ *             causal chain.  Ignored in flat mode.
  */
 typedef struct {
   int32_t mode;
@@ -109,6 +117,7 @@ typedef struct {
   int32_t max_prefix_len;
   const void* k_ext;
   const void* v_ext;
+  const uint8_t* draft_mask;
 } psattn_desc;
 
 /*

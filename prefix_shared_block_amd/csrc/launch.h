@@ -47,6 +47,7 @@ struct PagedArgs {
   int32_t split_len;
   float scale_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
+  const uint8_t* draft_mask;  // [B, L, L] draft visibility (nonzero: visible), or null: causal
 };
 
 // Backward of the flat forward (bf16).  Workspace: lse2 and delta [T, Hq]

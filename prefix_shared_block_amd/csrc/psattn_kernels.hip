@@ -620,14 +620,18 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
   for (int s = lane; s < a.n_splits; s += 64) mp = fmaxf(mp, a.part_lse[prow0 + (size_t)s * a.rows]);
   mp = wave_max(mp);
 
-  // draft block: keys 0..t of this request's draft K/V (causal), online softmax
+  // draft block: the draft keys row t sees (its draft-mask row, or 0..t),
+  // online softmax
   float q[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) q[e] = load_elem<QDT>(a.q, qrow * D + lane + 64 * e);
   float md = -__builtin_inff();
   float ld = 0.f;
   float od = 0.f;
-  for (int j = 0; j <= t; ++j) {
+  const uint8_t* mrow = a.draft_mask ? a.draft_mask + ((size_t)b * a.draft_len + t) * a.draft_len : nullptr;
+  const int jend = mrow ? a.draft_len : t + 1;
+  for (int j = 0; j < jend; ++j) {
+    if (mrow && mrow[j] == 0) continue;  // the same row for the whole wave
     const size_t krow = ((size_t)(b * a.draft_len + j) * a.hkv + h_kv) * D;
     float zz = 0.f;
 #pragma unroll
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
   const float mt = fmaxf(mp, lse_d);
   const float wd = fast_exp2(lse_d - mt);
   float wsum = wd;
-  float acc = od * (wd / ld);
+  float acc = ld > 0.f ? od * (wd / ld) : 0.f;
   const float* po = a.part_o + prow0 * D + dcol;
   const size_t sstride = (size_t)a.rows * D;
   int s = 0;

@@ -93,7 +93,9 @@ __device__ __forceinline__ void put_chunk(char* trow, int pos, int f, const u32x
 // W waves per workgroup, each streaming its own share of the split's stages
 // independently; OCC: waves per SIMD the register budget is held to (2 for
 // head dims up to 128, so that two independent streams share each SIMD).
-template <int D, int KDT, int OCC, int W>
+// TREE: the draft block follows the request's draft mask (a compile-time
+// variant, so that the causal kernel keeps its own code)
+template <int D, int KDT, int OCC, int W, bool TREE>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC)))
 void paged_reg_kernel(PagedArgs a) {
   using C = RCfg<D, KDT>;
@@ -140,6 +142,20 @@ void paged_reg_kernel(PagedArgs a) {
   // the same row stride as the slots of a page
   const size_t ext_off = ((size_t)b * a.draft_len * a.hkv + h_kv) * C::ROWB;
   const int trow = q16 / a.g;  // draft position of stacked row q16
+  // draft keys 4 g + e (e = 0..3) this lane's row sees: its draft-mask row,
+  // or the causal chain (keys 0 .. trow)
+  uint32_t dvis = 0;
+  if constexpr (TREE) {
+    const int tr = trow < a.draft_len ? trow : a.draft_len - 1;
+    const uint8_t* mrow = a.draft_mask + ((size_t)b * a.draft_len + tr) * a.draft_len;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * g + e;
+      const bool v = j < a.draft_len && mrow[j] != 0;
+      dvis |= (v ? 1u : 0u) << e;
+    }
+    asm volatile("" ::"v"(dvis));  // retired here, before the stage ring
+  }
 
   // ---- query fragments of row q16 (rows past R reuse row 0; never stored):
   // k-step s, lane group g holds head-dim elements 32 s + 8 g .. +8
@@ -226,12 +242,16 @@ void paged_reg_kernel(PagedArgs a) {
     }
     // ---- online softmax of the stage (prefix keys past kend, and draft keys
     // after the row's own draft position, are masked)
-    const int lim = n < npre ? kend - k0 : trow + 1;
+    const bool draft = n >= npre;
+    const int lim = !draft ? kend - k0 : trow + 1;
     float mr = -__builtin_inff();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float x = sc[e];
-      if (4 * g + e >= lim) x = -__builtin_inff();
+      bool hide;
+      if constexpr (TREE) hide = draft ? !((dvis >> e) & 1u) : (4 * g + e >= lim);
+      else hide = 4 * g + e >= lim;
+      if (hide) x = -__builtin_inff();
       sc[e] = x;
       mr = fmaxf(mr, x);
     }
@@ -420,7 +440,10 @@ template <int D, int KDT>
 int launch_t(const PagedArgs& a, int64_t n_blocks, hipStream_t s) {
   constexpr int OCC = D <= 128 ? 2 : 1;
   constexpr int W = reg_waves(D);
-  hipLaunchKernelGGL((paged_reg_kernel<D, KDT, OCC, W>), dim3((unsigned)n_blocks), dim3(64 * W), 0, s, a);
+  if (a.draft_mask)
+    hipLaunchKernelGGL((paged_reg_kernel<D, KDT, OCC, W, true>), dim3((unsigned)n_blocks), dim3(64 * W), 0, s, a);
+  else
+    hipLaunchKernelGGL((paged_reg_kernel<D, KDT, OCC, W, false>), dim3((unsigned)n_blocks), dim3(64 * W), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -83,7 +83,9 @@ __device__ __forceinline__ void wput(char* trow, int pos, int f, const u32x4_t x
   }
 }
 
-template <int D, int KDT>
+// TREE: the draft block follows the request's draft mask (a compile-time
+// variant, so that the causal kernel keeps its own code)
+template <int D, int KDT, bool TREE>
 __global__ __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void paged_wide_kernel(PagedArgs a) {
   using C = WCfg<D, KDT>;
@@ -119,6 +121,21 @@ void paged_wide_kernel(PagedArgs a) {
   const size_t ext_off = ((size_t)b * a.draft_len * a.hkv + h_kv) * C::ROWB;
   const int myrow = 16 * rq + q16;  // stacked row of this lane's scores
   const int trow = (myrow < a.rows ? myrow : 0) / a.g;
+  // draft keys 32 kh + 16 j + 4 g + e (j = 0, 1; e = 0..3) this lane's row
+  // sees: its draft-mask row, or the causal chain (keys 0 .. trow)
+  uint32_t dvis = 0;
+  if constexpr (TREE) {
+    const uint8_t* mrow = a.draft_mask + ((size_t)b * a.draft_len + trow) * a.draft_len;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 32 * kh + 16 * j + 4 * g + e;
+        const bool v = key < a.draft_len && mrow[key] != 0;
+        dvis |= (v ? 1u : 0u) << (4 * j + e);
+      }
+    asm volatile("" ::"v"(dvis));  // retired here, before the stage ring
+  }
 
   // ---- query fragments (B operand of S^T = K Q^T): row 16 rq + q16,
   // k-step s, lane group g holds head-dim elements 32 s + 8 g .. +8
@@ -204,7 +221,8 @@ void paged_wide_kernel(PagedArgs a) {
     // keys 32 kh .. 32 kh + 31 of superstage n; lim = keys of the half that
     // this lane's row may see
     const int kofs = 32 * kh;
-    const int lim = n < npre ? kend - (kbeg + 64 * n) - kofs : (trow + 1) - kofs;
+    const bool draft = n >= npre;
+    const int lim = !draft ? kend - (kbeg + 64 * n) - kofs : (trow + 1) - kofs;
     // ---- S^T blocks j = 0, 1 (16 keys x 16 rows): lane (q16, g) gets keys
     // 16 j + 4 g .. +3 of row q16
     f32x4_t sc[2];
@@ -225,7 +243,10 @@ void paged_wide_kernel(PagedArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = sc[j][e];
-        if (16 * j + 4 * g + e >= lim) x = -__builtin_inff();
+        bool hide;
+        if constexpr (TREE) hide = draft ? !((dvis >> (4 * j + e)) & 1u) : (16 * j + 4 * g + e >= lim);
+        else hide = 16 * j + 4 * g + e >= lim;
+        if (hide) x = -__builtin_inff();
         sc[j][e] = x;
         mr = fmaxf(mr, x);
       }
@@ -347,8 +368,12 @@ void paged_wide_kernel(PagedArgs a) {
 
 template <int D, int KDT>
 int launch_t(const PagedArgs& a, int64_t n_blocks, hipStream_t s) {
+  if (a.draft_mask) {
+    hipLaunchKernelGGL((paged_wide_kernel<D, KDT, true>), dim3((unsigned)n_blocks), dim3(64 * kWideWaves), 0, s, a);
+    return (int)hipGetLastError();
+  }
   static_assert(64 * D * 4 + 2 * 64 * 4 <= 4 * WCfg<D, KDT>::TILE, "merge area");
-  hipLaunchKernelGGL((paged_wide_kernel<D, KDT>), dim3((unsigned)n_blocks), dim3(64 * kWideWaves), 0, s, a);
+  hipLaunchKernelGGL((paged_wide_kernel<D, KDT, false>), dim3((unsigned)n_blocks), dim3(64 * kWideWaves), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -44,6 +44,7 @@ class PsattnDesc(ctypes.Structure):
         ("max_prefix_len", ctypes.c_int32),
         ("k_ext", ctypes.c_void_p),
         ("v_ext", ctypes.c_void_p),
+        ("draft_mask", ctypes.c_void_p),
     ]
 
 
@@ -167,7 +168,7 @@ def flat_desc(total_tokens: int, prefix_len: int, num_segments: int, seg_offsets
 
 def paged_desc(batch: int, draft_len: int, page_size: int, num_pages: int, prefix_lens_ptr: int,
                kv_indptr_ptr: int, kv_indices_ptr: int, max_prefix_len: int, k_ext_ptr: int,
-               v_ext_ptr: int) -> PsattnDesc:
+               v_ext_ptr: int, draft_mask_ptr: int = 0) -> PsattnDesc:
     d = PsattnDesc()
     d.mode = MODE_PAGED
     d.batch = int(batch)
@@ -180,6 +181,7 @@ def paged_desc(batch: int, draft_len: int, page_size: int, num_pages: int, prefi
     d.max_prefix_len = int(max_prefix_len)
     d.k_ext = k_ext_ptr or None
     d.v_ext = v_ext_ptr or None
+    d.draft_mask = draft_mask_ptr or None
     return d
 
 
@@ -263,10 +265,12 @@ def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: i
 
 def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext, draft_len: int,
               max_prefix_len: int, sm_scale: Optional[float] = None, k_scale: float = 1.0,
-              v_scale: float = 1.0, kv_dtype: Optional[int] = None, out=None, lse=None, workspace=None):
+              v_scale: float = 1.0, kv_dtype: Optional[int] = None, out=None, lse=None, workspace=None,
+              draft_mask=None):
     """Speculative-verify forward over a paged prefix.  q [B*Lx,Hq,D];
     pools [num_pages, page_size, Hkv, D]; k_ext/v_ext [B*Lx, Hkv, D]; index
-    arrays int32 on the device.  Returns (o, lse)."""
+    arrays int32 on the device; draft_mask: optional uint8 [B, Lx, Lx] draft
+    tree on the device (None: the causal chain).  Returns (o, lse)."""
     import torch
 
     rows, hq, d = q.shape
@@ -281,7 +285,7 @@ def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ex
     if lse is None:
         lse = torch.empty((rows, hq), dtype=torch.float32, device=q.device)
     desc = paged_desc(batch, draft_len, page_size, num_pages, _ptr(prefix_lens), _ptr(kv_indptr),
-                      _ptr(kv_indices), max_prefix_len, _ptr(k_ext), _ptr(v_ext))
+                      _ptr(kv_indices), max_prefix_len, _ptr(k_ext), _ptr(v_ext), _ptr(draft_mask))
     ws_bytes = psattn_workspace_size(desc, hq, hkv, d, qdt, kvdt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
