@@ -180,7 +180,8 @@ def gather_prefix(pool: np.ndarray, kv_indptr, kv_indices, prefix_len: int, b: i
 def attn_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext,
                draft_len: int, sm_scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
                q_dtype: int = 1, kv_dtype: int = 1, page_size: int = 16,
-               requests: Optional[Sequence[int]] = None, draft_mask: Optional[np.ndarray] = None):
+               requests: Optional[Sequence[int]] = None, draft_mask: Optional[np.ndarray] = None,
+               qo_indptr: Optional[Sequence[int]] = None):
     """Reference for speculative verify over a paged prefix.
 
     q: [B*Lx, Hq, D]; k_pool/v_pool: [num_pages, page_size, Hkv, D];
@@ -192,28 +193,36 @@ def attn_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_e
     ancestors and itself), and every prefix key as before.  The sglang page's
     verify takes such a custom mask over the draft part only (its prefix part is
     skipped); without it, row t sees draft keys 0..t.
+
+    qo_indptr: optional [B+1] ragged draft lengths: request b's draft rows (of
+    q, k_ext, v_ext and the outputs) are qo_indptr[b] .. qo_indptr[b+1], and
+    draft_mask (if any) is read in its top-left [n_b, n_b] corner.
     """
     qf = decode(q, q_dtype)
     lx = int(draft_len)
     bn = len(prefix_lens)
     hq, d = qf.shape[1], qf.shape[2]
-    o = np.full((bn * lx, hq, d), np.nan)
-    lse = np.full((bn * lx, hq), np.nan)
+    o = np.full((qf.shape[0], hq, d), np.nan)
+    lse = np.full((qf.shape[0], hq), np.nan)
     reqs = range(bn) if requests is None else requests
     for b in reqs:
         pl = int(prefix_lens[b])
+        r0 = int(qo_indptr[b]) if qo_indptr is not None else b * lx
+        n = int(qo_indptr[b + 1]) - r0 if qo_indptr is not None else lx
+        if n == 0:
+            continue
         kp = decode(gather_prefix(k_pool, kv_indptr, kv_indices, pl, b, page_size), kv_dtype)
         vp = decode(gather_prefix(v_pool, kv_indptr, kv_indices, pl, b, page_size), kv_dtype)
-        kd = decode(k_ext[b * lx:(b + 1) * lx], kv_dtype)
-        vd = decode(v_ext[b * lx:(b + 1) * lx], kv_dtype)
+        kd = decode(k_ext[r0:r0 + n], kv_dtype)
+        vd = decode(v_ext[r0:r0 + n], kv_dtype)
         kx = np.concatenate([kp, kd], axis=0) * k_scale
         vx = np.concatenate([vp, vd], axis=0) * v_scale
         if draft_mask is None:
-            pos = pl + np.arange(lx)
-            oo, ll = causal_attention(qf[b * lx:(b + 1) * lx], pos, kx, vx, sm_scale)
+            pos = pl + np.arange(n)
+            oo, ll = causal_attention(qf[r0:r0 + n], pos, kx, vx, sm_scale)
         else:
-            vis = np.concatenate([np.ones((lx, pl), dtype=bool), np.asarray(draft_mask[b]) != 0], axis=1)
-            oo, ll = masked_attention(qf[b * lx:(b + 1) * lx], vis, kx, vx, sm_scale)
-        o[b * lx:(b + 1) * lx] = oo
-        lse[b * lx:(b + 1) * lx] = ll
+            vis = np.concatenate([np.ones((n, pl), dtype=bool), np.asarray(draft_mask[b])[:n, :n] != 0], axis=1)
+            oo, ll = masked_attention(qf[r0:r0 + n], vis, kx, vx, sm_scale)
+        o[r0:r0 + n] = oo
+        lse[r0:r0 + n] = ll
     return o, lse

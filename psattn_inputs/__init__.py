@@ -149,6 +149,9 @@ class PagedInstance:
     sm_scale: float
     seed: int
     page_size: int = PAGE_SIZE
+    # ragged draft lengths: request b's draft rows are qo_indptr[b] .. qo_indptr[b+1]
+    # (draft_len is then their upper bound); None: b * draft_len .. (b + 1) * draft_len
+    qo_indptr: Optional[np.ndarray] = None
 
     @property
     def batch(self) -> int:
@@ -202,23 +205,34 @@ def make_flat_random_lens(prefix_len: int, n_seg: int, lo: int, hi: int, hq: int
 def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d: int,
                kv_dtype: int = BF16, seed: int = 0, num_pages: Optional[int] = None,
                scales: bool = False, poison_unused: bool = True,
-               sm_scale: Optional[float] = None, name: str = "paged") -> PagedInstance:
+               sm_scale: Optional[float] = None, name: str = "paged",
+               draft_lens: Optional[Sequence[int]] = None) -> PagedInstance:
+    """draft_lens: per-request draft lengths (ragged); draft_len is then taken
+    as their maximum and the draft rows are packed back to back."""
     rng = _rng(seed)
     prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
     b = int(prefix_lens.shape[0])
+    qo = None
+    n_rows = b * draft_len
+    if draft_lens is not None:
+        dl = np.asarray(draft_lens, dtype=np.int64)
+        qo = np.zeros(b + 1, dtype=np.int64)
+        qo[1:] = np.cumsum(dl)
+        n_rows = int(qo[-1])
+        draft_len = int(dl.max()) if dl.size else 0
     n_b = (prefix_lens + PAGE_SIZE - 1) // PAGE_SIZE
     used = int(n_b.sum())
     if num_pages is None:
         num_pages = max(used, 1)
     if num_pages < used:
         raise ValueError("pool too small")
-    q = _normal(rng, (b * draft_len, hq, d))
+    q = _normal(rng, (n_rows, hq, d))
     # prefix K/V drawn per used page (unused pages are poisoned), then placed
     kp = _normal(rng, (used, PAGE_SIZE, hkv, d))
     vp = _normal(rng, (used, PAGE_SIZE, hkv, d))
     perm = rng.permutation(num_pages).astype(np.int64)
-    kx = _normal(rng, (b * draft_len, hkv, d))
-    vx = _normal(rng, (b * draft_len, hkv, d))
+    kx = _normal(rng, (n_rows, hkv, d))
+    vx = _normal(rng, (n_rows, hkv, d))
     if scales:
         k_scale = float(rng.uniform(0.5, 2.0))
         v_scale = float(rng.uniform(0.5, 2.0))
@@ -253,7 +267,8 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
         prefix_lens=prefix_lens.astype(np.int32), k_ext=_encode(kx, kv_dtype),
         v_ext=_encode(vx, kv_dtype), draft_len=int(draft_len), hq=hq, hkv=hkv, d=d,
         q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
-        sm_scale=float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)), seed=seed)
+        sm_scale=float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)), seed=seed,
+        qo_indptr=None if qo is None else qo.astype(np.int32))
 
 
 # ---------------------------------------------------------------------------
