@@ -96,7 +96,15 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *             sees draft key j iff draft_mask[(b * draft_len + t) * draft_len
  *             + j] != 0, and every prefix key.  Each row must see itself (a
  *             tree row holds its ancestors and its own token).  NULL: the
- *             causal chain.  Ignored in flat mode.
+ *             causal chain.  Ignored in flat mode.  With qo_indptr the mask
+ *             keeps this padded layout; request b uses its first n_b rows and
+ *             columns.
+ *   qo_indptr (device, int32, batch + 1) or NULL: ragged draft lengths.
+ *             Request b's draft rows of q, o, lse, k_ext and v_ext are
+ *             qo_indptr[b] .. qo_indptr[b+1] (n_b of them, 0 <= n_b <=
+ *             draft_len, which is then the upper bound); draft row t sits at
+ *             position prefix_lens[b] + t.  NULL: n_b = draft_len for every
+ *             request and its rows start at b * draft_len.
  */
 typedef struct {
   int32_t mode;
@@ -118,6 +126,7 @@ typedef struct {
   const void* k_ext;
   const void* v_ext;
   const uint8_t* draft_mask;
+  const int32_t* qo_indptr;
 } psattn_desc;
 
 /*

@@ -48,6 +48,7 @@ struct PagedArgs {
   float scale_log2;  // sm_scale * k_scale * log2(e)
   float v_scale;
   const uint8_t* draft_mask;  // [B, L, L] draft visibility (nonzero: visible), or null: causal
+  const int32_t* qo_indptr;   // [B + 1] ragged draft rows, or null: draft_len rows per request
 };
 
 // Backward of the flat forward (bf16).  Workspace: lse2 and delta [T, Hq]

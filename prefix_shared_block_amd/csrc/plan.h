@@ -325,6 +325,16 @@ PS_HD int64_t dkdv_items_per_head_ub(int64_t prefix_len, int64_t total, int64_t 
   return pre + rtiles * cdiv64(max_seg, rc);
 }
 
+// Ragged draft lengths: request b's draft rows (of q, o, lse, k_ext, v_ext)
+// are qo_indptr[b] .. qo_indptr[b+1]; without qo_indptr every request has
+// draft_len rows at b * draft_len.
+PS_HD int32_t draft_base(const int32_t* qo_indptr, int32_t b, int32_t draft_len) {
+  return qo_indptr ? qo_indptr[b] : b * draft_len;
+}
+PS_HD int32_t draft_count(const int32_t* qo_indptr, int32_t b, int32_t draft_len) {
+  return qo_indptr ? qo_indptr[b + 1] - qo_indptr[b] : draft_len;
+}
+
 // ---------------------------------------------------------------- flat plan
 PS_HD int64_t flat_items_per_head_ub(int64_t prefix_len, int64_t total, int64_t nseg, int64_t tt) {
   return cdiv64(prefix_len, tt) + (total - prefix_len) / tt + nseg;

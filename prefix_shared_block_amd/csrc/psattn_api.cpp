@@ -263,6 +263,7 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
     a.scale_log2 = sm_scale * k_scale * log2e;
     a.v_scale = v_scale;
     a.draft_mask = desc->draft_mask;
+    a.qo_indptr = desc->qo_indptr;
     err = launch_paged(a, d, (int)q_dtype, (int)kv_dtype, p.pg, p.paged_blocks, stream);
   }
   if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));

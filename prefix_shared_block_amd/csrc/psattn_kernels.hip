@@ -477,6 +477,9 @@ void paged_split_kernel(PagedArgs a) {
                              a.prefix_lens);
   const int b = it.seg;
   const int h_kv = it.h_kv;
+  const int qbase = draft_base(a.qo_indptr, b, a.draft_len);  // the request's first draft row
+  const int qn = draft_count(a.qo_indptr, b, a.draft_len);    // and its number of draft rows
+  if (qn <= 0) return;                                         // a request without draft rows
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -487,11 +490,11 @@ void paged_split_kernel(PagedArgs a) {
   const int ks = wave / RB;
 
   const int r = rb * kWaveRows + c;  // stacked row: draft-token-major, heads interleaved
-  const bool valid = r < a.rows;
+  const bool valid = r < a.rows && r / a.g < qn;
   const int rc = valid ? r : 0;
   const int t = rc / a.g;
   const int hl = rc - t * a.g;
-  const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
+  const size_t qrow = (size_t)(qbase + t) * a.hq + h_kv * a.g + hl;
 
   QFrag<D, F32C> qf;
   if constexpr (F32C)
@@ -611,7 +614,10 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
   const int t = r / a.g;
   const int hl = r - t * a.g;
   const int head = h_kv * a.g + hl;
-  const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + head;
+  const int qbase = draft_base(a.qo_indptr, b, a.draft_len);
+  const int qn = draft_count(a.qo_indptr, b, a.draft_len);
+  if (t >= qn) return;  // past the request's draft rows
+  const size_t qrow = (size_t)(qbase + t) * a.hq + head;
   const int dcol = chunk * 64 + lane;
 
   // max over the splits' log-sum-exps (log2 domain)
@@ -629,10 +635,10 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a, float s
   float ld = 0.f;
   float od = 0.f;
   const uint8_t* mrow = a.draft_mask ? a.draft_mask + ((size_t)b * a.draft_len + t) * a.draft_len : nullptr;
-  const int jend = mrow ? a.draft_len : t + 1;
+  const int jend = mrow ? qn : t + 1;
   for (int j = 0; j < jend; ++j) {
     if (mrow && mrow[j] == 0) continue;  // the same row for the whole wave
-    const size_t krow = ((size_t)(b * a.draft_len + j) * a.hkv + h_kv) * D;
+    const size_t krow = ((size_t)(qbase + j) * a.hkv + h_kv) * D;
     float zz = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) zz += q[e] * load_elem<KDT>(a.k_ext, krow + lane + 64 * e);

@@ -109,6 +109,9 @@ void paged_reg_kernel(PagedArgs a) {
   const Item it = paged_item(blockIdx.x, a.hkv, a.n_splits, a.split_len, a.draft_len, a.prefix_lens);
   const int b = it.seg;
   const int h_kv = it.h_kv;
+  const int qb = draft_base(a.qo_indptr, b, a.draft_len);  // the request's first draft row
+  const int qn = draft_count(a.qo_indptr, b, a.draft_len);  // and its number of draft rows
+  if (qn <= 0) return;                                       // a request without draft rows
   const int wave = W == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   char (*tiles)[2][C::TILE] = tiles_all[wave];
   const int lane = threadIdx.x & 63;
@@ -140,18 +143,18 @@ void paged_reg_kernel(PagedArgs a) {
   const int nst = npre + (it.split == a.n_splits - 1 && wave == W - 1 ? 1 : 0);
   // draft block: row j of request b at k_ext + ((b L + j) Hkv + h_kv) * ROWB,
   // the same row stride as the slots of a page
-  const size_t ext_off = ((size_t)b * a.draft_len * a.hkv + h_kv) * C::ROWB;
+  const size_t ext_off = ((size_t)qb * a.hkv + h_kv) * C::ROWB;
   const int trow = q16 / a.g;  // draft position of stacked row q16
   // draft keys 4 g + e (e = 0..3) this lane's row sees: its draft-mask row,
   // or the causal chain (keys 0 .. trow)
   uint32_t dvis = 0;
   if constexpr (TREE) {
-    const int tr = trow < a.draft_len ? trow : a.draft_len - 1;
+    const int tr = trow < qn ? trow : qn - 1;
     const uint8_t* mrow = a.draft_mask + ((size_t)b * a.draft_len + tr) * a.draft_len;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = 4 * g + e;
-      const bool v = j < a.draft_len && mrow[j] != 0;
+      const bool v = j < qn && mrow[j] != 0;
       dvis |= (v ? 1u : 0u) << e;
     }
     asm volatile("" ::"v"(dvis));  // retired here, before the stage ring
@@ -161,10 +164,10 @@ void paged_reg_kernel(PagedArgs a) {
   // k-step s, lane group g holds head-dim elements 32 s + 8 g .. +8
   bf16x8_t qf[C::NSTEP];
   auto load_q = [&]() {
-    const int rc = q16 < a.rows ? q16 : 0;
+    const int rc = q16 < a.rows && q16 / a.g < qn ? q16 : 0;
     const int t = rc / a.g;
     const int hl = rc - t * a.g;
-    const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
+    const size_t qrow = (size_t)(qb + t) * a.hq + h_kv * a.g + hl;
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
 #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
@@ -192,7 +195,7 @@ void paged_reg_kernel(PagedArgs a) {
     } else if (m < nst) {
       kb = reinterpret_cast<const char*>(a.k_ext) + ext_off;
       vb = reinterpret_cast<const char*>(a.v_ext) + ext_off;
-      last = a.draft_len - 1;
+      last = qn - 1;
     } else {
       kb = vb = reinterpret_cast<const char*>(a.q);
       last = 0;
@@ -387,7 +390,8 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   const int b = rw / (a.rows * a.hkv);
   const int t = r / a.g;
   const int hl = r - t * a.g;
-  const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
+  if (t >= draft_count(a.qo_indptr, b, a.draft_len)) return;  // past the request's draft rows
+  const size_t qrow = (size_t)(draft_base(a.qo_indptr, b, a.draft_len) + t) * a.hq + h_kv * a.g + hl;
   const size_t prow0 = (((size_t)b * a.hkv + h_kv) * a.n_splits) * a.rows + r;
   const size_t sstride = (size_t)a.rows * D;
   const int col = 64 * ch + lane;

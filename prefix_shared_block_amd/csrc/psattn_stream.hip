@@ -103,6 +103,9 @@ void paged_stream_kernel(PagedArgs a) {
 
   const Item it = paged_item(blockIdx.x, a.hkv, a.n_splits, a.split_len, a.draft_len, a.prefix_lens);
   const int b = it.seg;
+  const int qbase = draft_base(a.qo_indptr, b, a.draft_len);  // the request's first draft row
+  const int qn = draft_count(a.qo_indptr, b, a.draft_len);    // and its number of draft rows
+  if (qn <= 0) return;                                         // a request without draft rows
   const int h_kv = it.h_kv;
   const int kbeg = it.r0_begin;
   const int kend = it.r0_end;
@@ -129,10 +132,10 @@ void paged_stream_kernel(PagedArgs a) {
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int r = (rg * NQB + qb) * 16 + q16;
-    const int rc = r < a.rows ? r : 0;
+    const int rc = r < a.rows && r / a.g < qn ? r : 0;
     const int t = rc / a.g;
     const int hl = rc - t * a.g;
-    const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
+    const size_t qrow = (size_t)(qbase + t) * a.hq + h_kv * a.g + hl;
     const u32x4_t* qp =
         reinterpret_cast<const u32x4_t*>(reinterpret_cast<const __bf16*>(a.q) + qrow * D + 8 * g);
 #pragma unroll

@@ -97,6 +97,9 @@ void paged_wide_kernel(PagedArgs a) {
   const Item it = paged_item(blockIdx.x, a.hkv, a.n_splits, a.split_len, a.draft_len, a.prefix_lens);
   const int b = it.seg;
   const int h_kv = it.h_kv;
+  const int qb = draft_base(a.qo_indptr, b, a.draft_len);  // the request's first draft row
+  const int qn = draft_count(a.qo_indptr, b, a.draft_len);  // and its number of draft rows
+  if (qn <= 0) return;                                       // a request without draft rows
   const int kbeg = it.r0_begin;
   const int kend = it.r0_end;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -118,7 +121,7 @@ void paged_wide_kernel(PagedArgs a) {
   const size_t head_off = (size_t)h_kv * C::ROWB;
   const int npre = (kend - kbeg + 63) >> 6;
   const int nst = npre + (it.split == a.n_splits - 1 ? 1 : 0);
-  const size_t ext_off = ((size_t)b * a.draft_len * a.hkv + h_kv) * C::ROWB;
+  const size_t ext_off = ((size_t)qb * a.hkv + h_kv) * C::ROWB;
   const int myrow = 16 * rq + q16;  // stacked row of this lane's scores
   const int trow = (myrow < a.rows ? myrow : 0) / a.g;
   // draft keys 32 kh + 16 j + 4 g + e (j = 0, 1; e = 0..3) this lane's row
@@ -131,7 +134,7 @@ void paged_wide_kernel(PagedArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = 32 * kh + 16 * j + 4 * g + e;
-        const bool v = key < a.draft_len && mrow[key] != 0;
+        const bool v = key < qn && mrow[key] != 0;
         dvis |= (v ? 1u : 0u) << (4 * j + e);
       }
     asm volatile("" ::"v"(dvis));  // retired here, before the stage ring
@@ -141,10 +144,10 @@ void paged_wide_kernel(PagedArgs a) {
   // k-step s, lane group g holds head-dim elements 32 s + 8 g .. +8
   bf16x8_t qf[C::NSTEP];
   auto load_q = [&]() {
-    const int rc = myrow < a.rows ? myrow : 0;
+    const int rc = myrow < a.rows && myrow / a.g < qn ? myrow : 0;
     const int t = rc / a.g;
     const int hl = rc - t * a.g;
-    const size_t qrow = (size_t)(b * a.draft_len + t) * a.hq + h_kv * a.g + hl;
+    const size_t qrow = (size_t)(qb + t) * a.hq + h_kv * a.g + hl;
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
 #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
@@ -172,7 +175,7 @@ void paged_wide_kernel(PagedArgs a) {
       const size_t base = ext_off + (size_t)(8 * wave) * slot_stride;
       kb = reinterpret_cast<const char*>(a.k_ext) + base;
       vb = reinterpret_cast<const char*>(a.v_ext) + base;
-      lastr = a.draft_len - 1 - 8 * wave;
+      lastr = qn - 1 - 8 * wave;
       if (lastr < 0) {  // no draft rows in this block: reread the first one
         kb = reinterpret_cast<const char*>(a.k_ext) + ext_off;
         vb = reinterpret_cast<const char*>(a.v_ext) + ext_off;

@@ -45,6 +45,7 @@ class PsattnDesc(ctypes.Structure):
         ("k_ext", ctypes.c_void_p),
         ("v_ext", ctypes.c_void_p),
         ("draft_mask", ctypes.c_void_p),
+        ("qo_indptr", ctypes.c_void_p),
     ]
 
 
@@ -168,7 +169,7 @@ def flat_desc(total_tokens: int, prefix_len: int, num_segments: int, seg_offsets
 
 def paged_desc(batch: int, draft_len: int, page_size: int, num_pages: int, prefix_lens_ptr: int,
                kv_indptr_ptr: int, kv_indices_ptr: int, max_prefix_len: int, k_ext_ptr: int,
-               v_ext_ptr: int, draft_mask_ptr: int = 0) -> PsattnDesc:
+               v_ext_ptr: int, draft_mask_ptr: int = 0, qo_indptr_ptr: int = 0) -> PsattnDesc:
     d = PsattnDesc()
     d.mode = MODE_PAGED
     d.batch = int(batch)
@@ -182,6 +183,7 @@ def paged_desc(batch: int, draft_len: int, page_size: int, num_pages: int, prefi
     d.k_ext = k_ext_ptr or None
     d.v_ext = v_ext_ptr or None
     d.draft_mask = draft_mask_ptr or None
+    d.qo_indptr = qo_indptr_ptr or None
     return d
 
 
@@ -266,16 +268,20 @@ def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: i
 def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext, draft_len: int,
               max_prefix_len: int, sm_scale: Optional[float] = None, k_scale: float = 1.0,
               v_scale: float = 1.0, kv_dtype: Optional[int] = None, out=None, lse=None, workspace=None,
-              draft_mask=None):
+              draft_mask=None, qo_indptr=None):
     """Speculative-verify forward over a paged prefix.  q [B*Lx,Hq,D];
     pools [num_pages, page_size, Hkv, D]; k_ext/v_ext [B*Lx, Hkv, D]; index
     arrays int32 on the device; draft_mask: optional uint8 [B, Lx, Lx] draft
-    tree on the device (None: the causal chain).  Returns (o, lse)."""
+    tree on the device (None: the causal chain); qo_indptr: optional int32
+    [B+1] ragged draft rows on the device, draft_len then being their upper
+    bound (q holds qo_indptr[B] rows).  Returns (o, lse)."""
     import torch
 
     rows, hq, d = q.shape
     num_pages, page_size, hkv, _ = k_pool.shape
     batch = int(prefix_lens.numel())
+    if qo_indptr is None and rows != batch * draft_len:
+        raise ValueError("q must hold batch * draft_len rows (or pass qo_indptr)")
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     kvdt = _dtype_code(k_pool, kv_dtype)
@@ -285,7 +291,8 @@ def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ex
     if lse is None:
         lse = torch.empty((rows, hq), dtype=torch.float32, device=q.device)
     desc = paged_desc(batch, draft_len, page_size, num_pages, _ptr(prefix_lens), _ptr(kv_indptr),
-                      _ptr(kv_indices), max_prefix_len, _ptr(k_ext), _ptr(v_ext), _ptr(draft_mask))
+                      _ptr(kv_indices), max_prefix_len, _ptr(k_ext), _ptr(v_ext), _ptr(draft_mask),
+                      _ptr(qo_indptr))
     ws_bytes = psattn_workspace_size(desc, hq, hkv, d, qdt, kvdt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)

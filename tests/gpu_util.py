@@ -81,9 +81,10 @@ def run_paged(lib, inst, dev="cuda", workspace=None, draft_mask=None):
     o, of = guarded_empty(q.shape, q.dtype, dev)
     lse, lf = guarded_empty((q.shape[0], q.shape[1]), torch.float32, dev)
     dm = None if draft_mask is None else torch.from_numpy(np.ascontiguousarray(draft_mask, dtype=np.uint8)).to(dev)
+    qo = None if getattr(inst, "qo_indptr", None) is None else i32(inst.qo_indptr)
     lib.fwd_paged(q, kp, vp, indptr, indices, plens, kx, vx, inst.draft_len, inst.max_prefix_len,
                   sm_scale=inst.sm_scale, k_scale=inst.k_scale, v_scale=inst.v_scale,
-                  kv_dtype=inst.kv_dtype, out=o, lse=lse, workspace=workspace, draft_mask=dm)
+                  kv_dtype=inst.kv_dtype, out=o, lse=lse, workspace=workspace, draft_mask=dm, qo_indptr=qo)
     torch.cuda.synchronize()
     assert guards_intact(of) and guards_intact(lf), "write outside the output tensors"
     return o, lse

@@ -41,10 +41,11 @@ def test_exports_every_declared_symbol(lib):
 
 def test_struct_layout_matches_header(lib):
     # offsets of the C struct (x86-64 SysV): int64 after int32 is 8-aligned
-    assert ctypes.sizeof(ps.PsattnDesc) == 112
+    assert ctypes.sizeof(ps.PsattnDesc) == 120
     assert ps.PsattnDesc.seg_offsets.offset == 24
     assert ps.PsattnDesc.k_ext.offset == 88
     assert ps.PsattnDesc.draft_mask.offset == 104
+    assert ps.PsattnDesc.qo_indptr.offset == 112
     assert ctypes.sizeof(ps.PsattnPlanInfo) == 32
 
 
