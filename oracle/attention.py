@@ -109,6 +109,56 @@ def build_kv(x: np.ndarray, prefix_len: int, seg_begin: int, seg_end: int) -> np
     return x[idx].copy()
 
 
+def chain_of(i: int, seg_parent) -> list:
+    """Segments from the root-most ancestor down to segment i (parents precede
+    their children; -1 is the shared prefix)."""
+    out = []
+    j = int(i)
+    while j >= 0:
+        out.append(j)
+        j = int(seg_parent[j])
+    return out[::-1]
+
+
+def attn_flat_tree(q, k, v, prefix_len: int, seg_offsets: Sequence[int], seg_parent: Sequence[int],
+                   sm_scale: float, dtype: int = 0):
+    """Multi-level prefix sharing on the flat buffer [P | S1 | ... | SN].
+
+    seg_parent[i] is the segment whose tokens segment i continues (-1: the
+    shared prefix itself), with seg_parent[i] < i.  Each segment is expanded
+    the build_kv way to [P | its ancestors' tokens, root-most first | its own
+    tokens] and run through ordinary causal attention; its own rows land at
+    their flat positions, and the prefix rows come from the prefix alone.
+    """
+    def dec(x):
+        return x if dtype is None else decode(x, dtype)
+
+    offs = [int(x) for x in seg_offsets]
+    t_n, hq, d = q.shape
+    p = int(prefix_len)
+    n = len(offs) - 1
+    if offs[0] != p or offs[-1] != t_n or any(b < a for a, b in zip(offs, offs[1:])):
+        raise ValueError("bad seg_offsets")
+    if any(not (-1 <= int(seg_parent[i]) < i) for i in range(n)):
+        raise ValueError("seg_parent[i] must lie in [-1, i)")
+    o = np.full((t_n, hq, d), np.nan)
+    lse = np.full((t_n, hq), np.nan)
+    if p > 0:
+        idx = np.arange(p)
+        oo, ll = causal_attention(dec(q[idx]), idx, dec(k[idx]), dec(v[idx]), sm_scale)
+        o[:p], lse[:p] = oo, ll
+    for i in range(n):
+        a, b = offs[i], offs[i + 1]
+        if b == a:
+            continue
+        idx = np.concatenate([np.arange(p)] + [np.arange(offs[j], offs[j + 1]) for j in chain_of(i, seg_parent)])
+        m = idx.size
+        own = np.arange(m - (b - a), m)  # positions of the segment's own tokens in its expansion
+        oo, ll = causal_attention(dec(q[idx[own]]), own, dec(k[idx]), dec(v[idx]), sm_scale)
+        o[a:b], lse[a:b] = oo, ll
+    return o, lse
+
+
 def attn_flat(q, k, v, prefix_len: int, seg_offsets: Sequence[int], sm_scale: float,
               dtype: int = 0, rows: Optional[Sequence[int]] = None, check_prefix: bool = False):
     """Reference for the flat-packed layout [P | S1 | ... | SN].
