@@ -75,6 +75,20 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *     prefix alone (then total_tokens == prefix_len and seg_offsets may be NULL).
  *   max_seg_len (host): an upper bound of every segment length; it is only
  *     used for validation of sizes, never for correctness.
+ *   seg_parent (device, int32, num_segments entries) or NULL: multi-level
+ *     sharing (the multi-level tree "chain" case that the PrefixSharing PR #50
+ *     page lists beside the flat GRPO case in its mask-construction section,
+ *     and plans as "multi-level tree support": rollouts that share a common
+ *     continuation of the prompt as well as the prompt).  seg_parent[i] = -1
+ *     means segment i continues the prefix
+ *     directly; otherwise seg_parent[i] = j with 0 <= j < i, and segment i
+ *     continues segment j.  A row of segment i then sees the prefix, every
+ *     token of each ancestor segment (j, its parent, ... up to the prefix),
+ *     and its own segment causally: ordinary causal attention over
+ *     [P | ancestors, root-most first | S_i].  Entries outside [-1, i) end
+ *     the ancestor walk there (no out-of-bounds read, no endless loop, but
+ *     those rows are then wrong).  NULL: one level (every parent is -1).
+ *     bf16 only, forward only; ignored in paged mode.
  *
  * Paged mode (speculative target-verify, uniform draft length):
  *   q, o      [batch * draft_len, Hq, D]; draft row t of request b is row
@@ -127,6 +141,8 @@ typedef struct {
   const void* v_ext;
   const uint8_t* draft_mask;
   const int32_t* qo_indptr;
+  /* flat, multi-level sharing */
+  const int32_t* seg_parent;
 } psattn_desc;
 
 /*

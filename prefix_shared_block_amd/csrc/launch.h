@@ -21,6 +21,7 @@ struct FlatArgs {
   int32_t g;
   int32_t tile_tokens;
   float scale_log2;  // sm_scale * log2(e)
+  const int32_t* seg_parent;  // [N] parent segment (-1: the prefix), or null: one level
 };
 
 struct PagedArgs {

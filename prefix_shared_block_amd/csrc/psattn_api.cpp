@@ -84,6 +84,8 @@ psattn_status check_common(const psattn_desc* d, int32_t hq, int32_t hkv, int32_
       return fail(PSATTN_E_INVAL, "num_segments * max_seg_len < total_tokens - prefix_len");
     if (plan->g > kWaves * kWaveRows)
       return fail(PSATTN_E_UNSUPPORTED, "GQA group %d exceeds %d stacked rows", plan->g, kWaves * kWaveRows);
+    if (d->seg_parent && !bfpair)
+      return fail(PSATTN_E_UNSUPPORTED, "seg_parent (multi-level sharing) takes bf16 only");
     plan->fg = flat_geom(plan->g, hd);
     const int64_t per_head =
         t == 0 ? 0 : flat_items_per_head_ub(d->prefix_len, t, d->num_segments, plan->fg.tile_tokens);
@@ -134,6 +136,7 @@ psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t h
   psattn_status st = check_common(d, hq, hkv, hd, dt, dt, &bp->base);
   if (st != PSATTN_OK) return st;
   if (dt != PSATTN_BF16) return fail(PSATTN_E_UNSUPPORTED, "the backward takes bf16 only");
+  if (d->seg_parent) return fail(PSATTN_E_UNSUPPORTED, "the backward covers one-level sharing only (seg_parent set)");
   if (hd != 128) return fail(PSATTN_E_UNSUPPORTED, "the backward takes head dim 128 only (got %d)", hd);
   if (bp->base.g > 64) return fail(PSATTN_E_UNSUPPORTED, "the backward takes GQA groups up to 64 (got %d)", bp->base.g);
   const int64_t t = d->total_tokens;
@@ -229,6 +232,7 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
     a.o = o;
     a.lse = lse;
     a.seg_offsets = desc->seg_offsets;
+    a.seg_parent = desc->num_segments > 0 ? desc->seg_parent : nullptr;
     a.prefix_len = desc->prefix_len;
     a.nseg = desc->num_segments;
     a.hq = hq;

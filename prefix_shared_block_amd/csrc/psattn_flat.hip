@@ -62,7 +62,13 @@ struct F2Cfg {
   __device__ static constexpr int fv(int r) { return CPR >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-template <int D>
+// CHAIN: multi-level sharing (PrefixSharing PR #50, mask construction, the
+// multi-level tree "chain" case: a rollout continues a parent segment, which
+// may continue another).  After the prefix and the item's own range, one more
+// pass per ancestor segment walks that segment's keys, all visible, carrying
+// the online-softmax state.  A compile-time variant, so that one-level
+// sharing keeps its own code.
+template <int D, bool CHAIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(F2Cfg<D>::MINB)))
 void flat2_kernel(FlatArgs a) {
   using C = F2Cfg<D>;
@@ -101,30 +107,33 @@ void flat2_kernel(FlatArgs a) {
   // Tiles of a range that are whole and end at or before the item's first
   // query token are visible to every row: they form a leading run of the
   // range.  They are walked first (no mask), then the rest of both ranges.
-  const int n0 = cdiv32(it.r0_end - it.r0_begin, BN);
-  const int n1 = cdiv32(it.r1_end - it.r1_begin, BN);
-  const int nt = n0 + n1;
+  // (With CHAIN, later passes put an ancestor segment's range in r0 and
+  // leave r1 empty.)
+  int r0b = it.r0_begin, r0e = it.r0_end, r1b = it.r1_begin, r1e = it.r1_end;
+  int n0 = cdiv32(r0e - r0b, BN);
+  int n1 = cdiv32(r1e - r1b, BN);
+  int nt = n0 + n1;
   auto n_clean = [&](int b, int e) __attribute__((always_inline)) {
     const int whole = (e - b) / BN;
     const int causal = it.q_begin + 1 - b >= 0 ? (it.q_begin + 1 - b) / BN : 0;
     return whole < causal ? whole : causal;
   };
-  const int c0 = n0 > 0 ? n_clean(it.r0_begin, it.r0_end) : 0;
-  const int c1 = n1 > 0 ? n_clean(it.r1_begin, it.r1_end) : 0;
-  const int nc = c0 + c1;
+  int c0 = n0 > 0 ? n_clean(r0b, r0e) : 0;
+  int c1 = n1 > 0 ? n_clean(r1b, r1e) : 0;
+  int nc = c0 + c1;
   auto tile_range = [&](int n, int& k0, int& ke) __attribute__((always_inline)) {
     if (n < c0) {
-      k0 = it.r0_begin + n * BN;
-      ke = it.r0_end;
+      k0 = r0b + n * BN;
+      ke = r0e;
     } else if (n < nc) {
-      k0 = it.r1_begin + (n - c0) * BN;
-      ke = it.r1_end;
+      k0 = r1b + (n - c0) * BN;
+      ke = r1e;
     } else if (n < nc + n0 - c0) {
-      k0 = it.r0_begin + (n - c1) * BN;
-      ke = it.r0_end;
+      k0 = r0b + (n - c1) * BN;
+      ke = r0e;
     } else {
-      k0 = it.r1_begin + (n - n0) * BN;
-      ke = it.r1_end;
+      k0 = r1b + (n - n0) * BN;
+      ke = r1e;
     }
   };
 
@@ -275,21 +284,45 @@ void flat2_kernel(FlatArgs a) {
   // with explicit vmcnt counts that the compiler does not know about
 #pragma unroll
   for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(qf[s]));
-  if (nt > 0) issue(0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
-  int n = 0;
-  for (; n < nc; ++n) {
-    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    compute(n, std::false_type{});
+  int anc = CHAIN && it.kind == kFlatSuffix && a.seg_parent ? a.seg_parent[it.seg] : -1;
+  int child = it.seg;
+  for (;;) {
+    if (nt > 0) issue(0, 0);
     wait_vmcnt<0>();
     __syncthreads();
-  }
-  for (; n < nt; ++n) {
-    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    compute(n, std::true_type{});
-    wait_vmcnt<0>();
-    __syncthreads();
+    int n = 0;
+    for (; n < nc; ++n) {
+      if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+      compute(n, std::false_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    for (; n < nt; ++n) {
+      if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+      compute(n, std::true_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if constexpr (!CHAIN) {
+      break;
+    } else {
+      // the next ancestor segment.  A parent precedes its child and -1 is
+      // the prefix, already walked; an entry outside [-1, child) ends the
+      // walk, so the loop always ends and never reads outside seg_offsets.
+      anc = __builtin_amdgcn_readfirstlane(anc);
+      if (anc < 0 || anc >= child) break;
+      child = anc;
+      r0b = __builtin_amdgcn_readfirstlane(a.seg_offsets[anc]);
+      r0e = __builtin_amdgcn_readfirstlane(a.seg_offsets[anc + 1]);
+      r1b = r1e = 0;
+      anc = a.seg_parent[anc];
+      n0 = cdiv32(r0e - r0b, BN);
+      n1 = 0;
+      nt = n0;
+      c0 = n0 > 0 ? n_clean(r0b, r0e) : 0;
+      c1 = 0;
+      nc = c0;
+    }
   }
 
   // ---- epilogue.  O = acc / l goes through LDS so that every global store
@@ -333,7 +366,10 @@ void flat2_kernel(FlatArgs a) {
 
 template <int D>
 int launch_t(const FlatArgs& a, int64_t n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL((flat2_kernel<D>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, a);
+  if (a.seg_parent)
+    hipLaunchKernelGGL((flat2_kernel<D, true>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((flat2_kernel<D, false>), dim3((unsigned)n_blocks), dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -46,6 +46,7 @@ class PsattnDesc(ctypes.Structure):
         ("v_ext", ctypes.c_void_p),
         ("draft_mask", ctypes.c_void_p),
         ("qo_indptr", ctypes.c_void_p),
+        ("seg_parent", ctypes.c_void_p),
     ]
 
 
@@ -156,7 +157,7 @@ def check(status: int):
 
 # ------------------------------------------------------------------ descriptors
 def flat_desc(total_tokens: int, prefix_len: int, num_segments: int, seg_offsets_ptr: int,
-              max_seg_len: int) -> PsattnDesc:
+              max_seg_len: int, seg_parent_ptr: int = 0) -> PsattnDesc:
     d = PsattnDesc()
     d.mode = MODE_FLAT
     d.total_tokens = int(total_tokens)
@@ -164,6 +165,7 @@ def flat_desc(total_tokens: int, prefix_len: int, num_segments: int, seg_offsets
     d.num_segments = int(num_segments)
     d.seg_offsets = seg_offsets_ptr or None
     d.max_seg_len = int(max_seg_len)
+    d.seg_parent = seg_parent_ptr or None
     return d
 
 
@@ -213,10 +215,12 @@ def _ptr(t) -> int:
 
 
 def fwd_flat(q, k, v, prefix_len: int, seg_offsets, max_seg_len: int, sm_scale: Optional[float] = None,
-             out=None, lse=None):
+             out=None, lse=None, seg_parent=None):
     """Flat-packed [P | S1 .. SN] forward.  q [T,Hq,D], k/v [T,Hkv,D] contiguous
     on one GPU; seg_offsets: int32 device tensor with N+1 entries; max_seg_len:
-    host upper bound of the segment lengths.  Returns (o, lse)."""
+    host upper bound of the segment lengths; seg_parent: optional int32
+    device tensor of N parent segments (-1: the prefix) for multi-level
+    sharing.  Returns (o, lse)."""
     import torch
 
     t_n, hq, d = q.shape
@@ -228,7 +232,9 @@ def fwd_flat(q, k, v, prefix_len: int, seg_offsets, max_seg_len: int, sm_scale: 
     if lse is None:
         lse = torch.empty((t_n, hq), dtype=torch.float32, device=q.device)
     n = int(seg_offsets.numel()) - 1 if seg_offsets is not None else 0
-    desc = flat_desc(t_n, prefix_len, n, _ptr(seg_offsets), max_seg_len)
+    if seg_parent is not None and int(seg_parent.numel()) != n:
+        raise ValueError(f"seg_parent has {int(seg_parent.numel())} entries, {n} segments")
+    desc = flat_desc(t_n, prefix_len, n, _ptr(seg_offsets), max_seg_len, _ptr(seg_parent))
     qdt = _dtype_code(q)
     st = psattn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), desc, hq, hkv, d, float(sm_scale),
                     qdt, _dtype_code(k), 1.0, 1.0, 0, 0, _stream_handle(q.device))

@@ -334,6 +334,18 @@ def make_tree_mask(batch: int, draft_len: int, seed: int, chain: bool = False) -
     return m
 
 
+def make_seg_parents(n_seg: int, seed: int, root_frac: float = 0.3) -> np.ndarray:
+    """Seeded multi-level sharing structure: segment i continues the prefix
+    (-1) with probability root_frac (always for i = 0), else an earlier
+    segment drawn uniformly.  int32 [N]."""
+    rng = _rng(seed)
+    par = np.full(n_seg, -1, dtype=np.int32)
+    for i in range(1, n_seg):
+        if rng.random() >= root_frac:
+            par[i] = int(rng.integers(0, i))
+    return par
+
+
 def make_config(name: str, seed: Optional[int] = None):
     if name == "tiny":
         return make_flat(64, [16, 16], 2, 2, 64, dtype=F32, seed=1 if seed is None else seed,

@@ -41,11 +41,12 @@ def test_exports_every_declared_symbol(lib):
 
 def test_struct_layout_matches_header(lib):
     # offsets of the C struct (x86-64 SysV): int64 after int32 is 8-aligned
-    assert ctypes.sizeof(ps.PsattnDesc) == 120
+    assert ctypes.sizeof(ps.PsattnDesc) == 128
     assert ps.PsattnDesc.seg_offsets.offset == 24
     assert ps.PsattnDesc.k_ext.offset == 88
     assert ps.PsattnDesc.draft_mask.offset == 104
     assert ps.PsattnDesc.qo_indptr.offset == 112
+    assert ps.PsattnDesc.seg_parent.offset == 120
     assert ctypes.sizeof(ps.PsattnPlanInfo) == 32
 
 
@@ -96,6 +97,15 @@ def test_flat_validation(lib, kw, status):
 ])
 def test_flat_descriptor_validation(lib, desc_kw, status):
     assert _call(_flat(**desc_kw)) == status
+
+
+def test_seg_parent_takes_bf16_forward_only(lib):
+    # multi-level sharing: the bf16 kernel only; fp32 and the backward refuse it
+    d = ps.flat_desc(96, 64, 2, FAKE, 16, seg_parent_ptr=FAKE)
+    assert _call(d, qdt=ps.F32, kvdt=ps.F32) == ps.E_UNSUPPORTED
+    assert "seg_parent" in ps.psattn_last_error()
+    assert _bwd(d) == ps.E_UNSUPPORTED
+    assert "seg_parent" in ps.psattn_last_error()
 
 
 def test_flat_gqa_group_too_large(lib):
