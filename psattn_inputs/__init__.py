@@ -17,6 +17,9 @@ and EAGLE top-k=1 target-verify over a paged KV cache):
   D=256, K/V stored as fp8 e4m3fn with per-tensor scales in [0.5, 2].
 * ``grpo_ragged`` P=8192, N=16 suffixes with lengths uniform in [256, 1024],
   Hq=64, Hkv=8, D=128, bf16, 1% of key rows scaled by 8 (outlier logits).
+* ``mla_dsa``   sparse shared-latent MLA prefill: 16384 prompt tokens, 64
+  heads reading one 512-wide latent row per cached token, top-2048 index
+  lists (``make_mla``), bf16.
 
 Draw order inside one instance (fixed, so a seed names the bytes):
 segment lengths -> Q -> K -> V -> outlier rows -> page permutation ->
@@ -334,6 +337,85 @@ def make_tree_mask(batch: int, draft_len: int, seed: int, chain: bool = False) -
     return m
 
 
+@dataclasses.dataclass
+class MlaInstance:
+    """Sparse shared-latent MLA instance (DSA prefill layout).
+
+    q: [T, H, D] bf16 bits; ckv: [S, D] bf16 bits, one latent row per cached
+    token (key and value alike); indices: int32 [T, topk], -1 = padding;
+    sink: optional float32 [H] per-head logits."""
+
+    name: str
+    q: np.ndarray
+    ckv: np.ndarray
+    indices: np.ndarray
+    sink: Optional[np.ndarray]
+    sm_scale: float
+    seed: int
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_heads(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def dim(self) -> int:
+        return int(self.q.shape[2])
+
+    @property
+    def topk(self) -> int:
+        return int(self.indices.shape[1])
+
+
+def make_mla_indices(num_tokens: int, topk: int, seed: int, num_kv: Optional[int] = None,
+                     scatter_pad: bool = False) -> np.ndarray:
+    """Seeded top-k index lists of a causal prefill: token t names
+    min(t + 1, topk) distinct cached positions drawn uniformly from [0, t]
+    (every position when there are at most topk of them), in random order,
+    then -1 padding (scattered through the row with scatter_pad).  With
+    num_kv the positions are drawn from [0, num_kv) instead of [0, t]."""
+    rng = _rng(seed)
+    out = np.full((num_tokens, topk), -1, dtype=np.int32)
+    for t in range(num_tokens):
+        pool = (t + 1) if num_kv is None else num_kv
+        n = min(pool, topk)
+        if n == 0:
+            continue
+        pick = rng.permutation(pool)[:n] if pool <= 4 * topk else _distinct(rng, pool, n)
+        out[t, :n] = pick
+        if scatter_pad:
+            out[t] = out[t, rng.permutation(topk)]
+    return out
+
+
+def _distinct(rng: np.random.Generator, pool: int, n: int) -> np.ndarray:
+    # n distinct integers of [0, pool), uniformly, in random order (draws with
+    # rejection of repeats; pool > 4 n, so a few rounds suffice)
+    got = np.unique(rng.integers(0, pool, size=n + n // 4 + 8))
+    while got.size < n:
+        got = np.union1d(got, rng.integers(0, pool, size=n))
+    got = rng.permutation(got)[:n]
+    return got
+
+
+def make_mla(num_tokens: int, num_heads: int, dim: int, topk: int, seed: int = 0, sink: bool = False,
+             num_kv: Optional[int] = None, scatter_pad: bool = False, sm_scale: Optional[float] = None,
+             name: str = "mla") -> MlaInstance:
+    """Draw order: indices, Q, latent cache, sink.  The cache holds the
+    prompt's own latent rows (S = num_tokens) unless num_kv is given."""
+    s_n = num_tokens if num_kv is None else num_kv
+    idx = make_mla_indices(num_tokens, topk, seed, num_kv=num_kv, scatter_pad=scatter_pad)
+    rng = _rng(seed * 7919 + 1)
+    q = _normal(rng, (num_tokens, num_heads, dim))
+    c = _normal(rng, (s_n, dim))
+    sk = _normal(rng, (num_heads,)) if sink else None
+    return MlaInstance(name=name, q=f32_to_bf16_bits(q), ckv=f32_to_bf16_bits(c), indices=idx, sink=sk,
+                       sm_scale=float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(dim)), seed=seed)
+
+
 def make_seg_parents(n_seg: int, seed: int, root_frac: float = 0.3) -> np.ndarray:
     """Seeded multi-level sharing structure: segment i continues the prefix
     (-1) with probability root_frac (always for i = 0), else an earlier
@@ -360,6 +442,8 @@ def make_config(name: str, seed: Optional[int] = None):
         return make_paged([32768] * 4, 8, 16, 2, 256, kv_dtype=FP8,
                           seed=4 if seed is None else seed, num_pages=16384, scales=True,
                           name=name)
+    if name == "mla_dsa":
+        return make_mla(16384, 64, 512, 2048, seed=6 if seed is None else seed, name=name)
     if name == "grpo_ragged":
         inst = make_flat_random_lens(8192, 16, 256, 1024, 64, 8, 128, dtype=BF16,
                                      seed=5 if seed is None else seed, outlier_frac=0.01)
