@@ -132,6 +132,44 @@ class FlatRunner:
             raise RuntimeError(f"{self.inst.name}: non-finite output")
 
 
+class MlaRunner:
+    """The sparse shared-latent MLA forward at one instance."""
+
+    def __init__(self, ps, inst):
+        import torch
+
+        self.ps, self.inst = ps, inst
+        self.q = torch.from_numpy(inst.q.view(np.int16)).view(torch.bfloat16).cuda()
+        self.ckv = torch.from_numpy(inst.ckv.view(np.int16)).view(torch.bfloat16).cuda()
+        self.idx = torch.from_numpy(inst.indices).cuda()
+        self.sink = None if inst.sink is None else torch.from_numpy(inst.sink.astype(np.float32)).cuda()
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+        self.n_keys = int(((inst.indices >= 0) & (inst.indices < inst.ckv.shape[0])).sum())
+
+    def __call__(self):
+        self.ps.fwd_mla(self.q, self.ckv, self.idx, sm_scale=self.inst.sm_scale, sink=self.sink, out=self.o,
+                        lse=self.lse)
+
+    def useful_flops(self) -> float:
+        # 4 * D per (token, head, listed key): the score and value products
+        return 4.0 * self.inst.dim * self.inst.num_heads * self.n_keys
+
+    def gathered_bytes(self) -> float:
+        # every listed latent row once per token (2 * D bytes), plus Q and O
+        return float(self.n_keys * 2 * self.inst.dim + 2 * self.q.numel() * 2)
+
+    def check(self):
+        import torch
+
+        self()
+        torch.cuda.synchronize()
+        ok = bool(torch.isfinite(self.o).all().item() and torch.isfinite(self.lse).all().item())
+        log(f"{self.inst.name}: outputs finite: {ok}")
+        if not ok:
+            raise RuntimeError(f"{self.inst.name}: non-finite output")
+
+
 class BwdRunner:
     """The flat backward at one instance: forward outputs computed once, then
     each call runs psattn_bwd (row terms, dQ, dK/dV, conversion)."""
@@ -451,6 +489,22 @@ def main():
                              "frac_mfma": round(cf / (tc["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                              "parents": parents}
         del cr
+
+    if args.all:
+        # sparse shared-latent MLA (DSA prefill): 16384 tokens, 64 heads,
+        # top-2048 lists over the prompt's own 512-wide latent rows
+        log("generating mla_dsa workload")
+        m_inst = make_config("mla_dsa")
+        mr = MlaRunner(ps, m_inst)
+        if not args.no_check:
+            mr.check()
+        tm = time_calls(mr, flush, max(5, args.steps // 3), 2)
+        mf = mr.useful_flops()
+        mb = mr.gathered_bytes()
+        out["mla_dsa"] = {"ms": round(tm["mean"], 4), "useful_tflops": round(mf / (tm["mean"] * 1e-3) / 1e12, 2),
+                          "frac_mfma": round(mf / (tm["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "gathered_gbs": round(mb / (tm["mean"] * 1e-3) / 1e9, 1)}
+        del mr
 
     if args.copy_calib:
         n = (256 << 20) // 4

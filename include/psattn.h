@@ -240,6 +240,37 @@ psattn_status psattn_bwd(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Sparse shared-latent MLA forward (DSA / sparse-MLA prefill; the vLLM issue
+ * "[Perf] SM8x sparse-MLA prefill fallback re-reads the shared MLA latent
+ * once per head", sections 适用环境 and 原因分析): every query token attends
+ * to the cached tokens its top-k list names, and all of its heads read the
+ * same latent rows, which serve as keys and values (the NoPE layout,
+ * kv_lora_rank = 512, no rope part).  One workgroup stacks all heads of a
+ * token, so each gathered latent row is read once per token, not per head.
+ *   q       : [num_tokens, num_heads, dim] bf16, device, 16-byte aligned.
+ *   ckv     : the latent cache, num_kv rows of kv_stride bf16 elements (the
+ *             first dim used), device, 16-byte aligned; the buffer must hold
+ *             (num_kv - 1) * kv_stride + dim elements.
+ *   indices : [num_tokens, topk] int32, device: cache rows token t attends
+ *             to, once per entry (an entry listed twice counts twice).
+ *             Entries outside [0, num_kv), such as -1 padding, are skipped.
+ *   sink    : [num_heads] fp32 natural-log logits, device, or NULL: sink_h
+ *             joins head h's softmax normaliser and carries no value.
+ *   o, lse  : outputs [num_tokens, num_heads, dim] bf16 and [num_tokens,
+ *             num_heads] fp32 (natural log).  o[t, h] = sum_j e^{z_j} c_j /
+ *             (sum_j e^{z_j} + e^{sink_h}), z_j = sm_scale <q[t, h], c_j>,
+ *             lse = ln of that denominator.  A token with no valid entry
+ *             gets o = 0 and lse = sink_h, or -inf without sinks.
+ *   dim = 512; num_heads in {32, 64, 128}; 0 <= topk <= 2048; kv_stride >=
+ *   dim, a multiple of 8; dtype PSATTN_BF16.  Allocates nothing; one launch
+ *   on `stream`.  Other configurations return PSATTN_E_UNSUPPORTED or
+ *   PSATTN_E_INVAL with nothing enqueued.
+ */
+psattn_status psattn_mla_fwd(const void* q, const void* ckv, const int32_t* indices, const float* sink, void* o,
+                             float* lse, int64_t num_tokens, int32_t num_heads, int32_t dim, int64_t num_kv,
+                             int32_t kv_stride, int32_t topk, float sm_scale, psattn_dtype dtype, void* stream);
+
+/*
  * Test hook: run the segment planner ON THE DEVICE for every workgroup of the
  * prefix-pass launch psattn_fwd would make and write its work items
  * (PSATTN_ITEM_FIELDS int32 each, in workgroup order) to items_dev, which

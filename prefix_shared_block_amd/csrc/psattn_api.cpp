@@ -10,6 +10,7 @@
 
 #include "../../include/psattn.h"
 #include "launch.h"
+#include "mla.h"
 #include "plan.h"
 
 using namespace psattn;
@@ -329,6 +330,49 @@ psattn_status psattn_bwd(const void* q, const void* k, const void* v, const void
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.sm_scale = sm_scale;
   const int err = launch_flat_bwd(a, d, bp.dq_blocks, bp.dkdv_blocks, stream);
+  if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
+  return PSATTN_OK;
+}
+
+psattn_status psattn_mla_fwd(const void* q, const void* ckv, const int32_t* indices, const float* sink, void* o,
+                             float* lse, int64_t num_tokens, int32_t num_heads, int32_t dim, int64_t num_kv,
+                             int32_t kv_stride, int32_t topk, float sm_scale, psattn_dtype dtype, void* stream) {
+  g_last_error.clear();
+  if ((int)dtype < 0 || (int)dtype > 2) return fail(PSATTN_E_INVAL, "unknown dtype code %d", (int)dtype);
+  if (dtype != PSATTN_BF16) return fail(PSATTN_E_UNSUPPORTED, "the sparse MLA forward takes bf16 only");
+  if (dim != kMlaDim) return fail(PSATTN_E_UNSUPPORTED, "latent width %d is not %d", dim, kMlaDim);
+  if (num_heads != 32 && num_heads != 64 && num_heads != 128)
+    return fail(PSATTN_E_UNSUPPORTED, "num_heads %d not in {32, 64, 128}", num_heads);
+  if (num_tokens < 0 || num_tokens > INT32_MAX)
+    return fail(PSATTN_E_INVAL, "num_tokens %lld out of range", (long long)num_tokens);
+  if (num_kv < 0 || num_kv > INT32_MAX) return fail(PSATTN_E_INVAL, "num_kv %lld out of range", (long long)num_kv);
+  if (topk < 0) return fail(PSATTN_E_INVAL, "topk %d < 0", topk);
+  if (topk > kMlaMaxTopk) return fail(PSATTN_E_UNSUPPORTED, "topk %d exceeds %d", topk, kMlaMaxTopk);
+  if (kv_stride < dim || kv_stride % 8 != 0)
+    return fail(PSATTN_E_INVAL, "kv_stride %d must be >= %d and a multiple of 8", kv_stride, dim);
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(PSATTN_E_INVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (num_tokens == 0) return PSATTN_OK;
+  if (!q || !o || !lse) return fail(PSATTN_E_INVAL, "q, o and lse must not be NULL");
+  if (topk > 0 && !indices) return fail(PSATTN_E_INVAL, "indices must not be NULL");
+  if (num_kv > 0 && !ckv) return fail(PSATTN_E_INVAL, "ckv must not be NULL");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(ckv, 16) || !aligned(lse, 4) || !aligned(indices, 4) ||
+      !aligned(sink, 4))
+    return fail(PSATTN_E_INVAL, "q, o and ckv must be 16-byte aligned; lse, indices and sink 4-byte aligned");
+  MlaArgs a{};
+  a.q = q;
+  a.ckv = ckv;
+  a.indices = indices;
+  a.sink = sink;
+  a.o = o;
+  a.lse = lse;
+  a.num_tokens = (int32_t)num_tokens;
+  a.num_heads = num_heads;
+  a.num_kv = (int32_t)num_kv;
+  a.kv_stride = kv_stride;
+  a.topk = topk;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const int err = launch_mla_sparse(a, stream);
   if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
   return PSATTN_OK;
 }

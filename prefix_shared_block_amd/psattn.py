@@ -95,6 +95,8 @@ def load(path: Optional[str] = None):
     lib.psattn_bwd_workspace_size.restype = sz
     lib.psattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, dp, i32, i32, i32, f32, i32, vp, sz, vp]
     lib.psattn_bwd.restype = i32
+    lib.psattn_mla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, f32, i32, vp]
+    lib.psattn_mla_fwd.restype = i32
     lib.psattn_status_string.argtypes = [i32]
     lib.psattn_status_string.restype = ctypes.c_char_p
     lib.psattn_last_error.argtypes = []
@@ -136,6 +138,12 @@ def psattn_bwd(q: int, k: int, v: int, o: int, lse: int, dout: int, dq: int, dk:
                workspace_bytes: int, stream: int) -> int:
     return int(load().psattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, _ref(desc), hq, hkv, d, sm_scale, dtype,
                                  workspace, workspace_bytes, stream))
+
+
+def psattn_mla_fwd(q: int, ckv: int, indices: int, sink: int, o: int, lse: int, num_tokens: int, num_heads: int,
+                   dim: int, num_kv: int, kv_stride: int, topk: int, sm_scale: float, dtype: int, stream: int) -> int:
+    return int(load().psattn_mla_fwd(q, ckv, indices, sink, o, lse, num_tokens, num_heads, dim, num_kv, kv_stride,
+                                     topk, sm_scale, dtype, stream))
 
 
 def psattn_plan_dump(desc: PsattnDesc, hq: int, hkv: int, d: int, q_dtype: int, kv_dtype: int,
@@ -269,6 +277,30 @@ def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: i
                     hq, hkv, d, float(sm_scale), dt, _ptr(workspace), wsz, _stream_handle(q.device))
     check(st)
     return dq, dk, dv
+
+
+def fwd_mla(q, ckv, indices, sm_scale: Optional[float] = None, sink=None, out=None, lse=None):
+    """Sparse shared-latent MLA forward.  q [T, H, 512] bf16; ckv [S, stride]
+    bf16 latent rows (the first 512 used); indices int32 [T, topk] (-1 or any
+    entry outside [0, S) skipped); sink: optional fp32 [H].  Returns (o, lse)."""
+    import torch
+
+    t_n, hq, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if ckv.dim() != 2 or ckv.stride(1) != 1:
+        raise ValueError("ckv must be [S, stride] with unit column stride")
+    if indices.dim() != 2 or indices.shape[0] != t_n or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous [T, topk] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((t_n, hq), dtype=torch.float32, device=q.device)
+    st = psattn_mla_fwd(_ptr(q), _ptr(ckv), _ptr(indices), _ptr(sink), _ptr(out), _ptr(lse), t_n, hq, d,
+                        int(ckv.shape[0]), int(ckv.stride(0)), int(indices.shape[1]), float(sm_scale),
+                        _dtype_code(q), _stream_handle(q.device))
+    check(st)
+    return out, lse
 
 
 def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext, draft_len: int,

@@ -279,3 +279,38 @@ def test_bwd_workspace_size(lib):
 
 def test_bwd_empty_enqueues_nothing(lib):
     assert _bwd(ps.flat_desc(0, 0, 0, 0, 0), ptr=0, lse=0, ws=0, wsb=0) == ps.OK
+
+
+# ------------------------------------------------------------------ sparse MLA
+def _mla(q=FAKE, ckv=FAKE, idx=FAKE, sink=0, o=FAKE, lse=FAKE, t=16, h=64, d=512, s=100, stride=512, topk=32,
+         sm=0.04, dt=ps.BF16):
+    return ps.psattn_mla_fwd(q, ckv, idx, sink, o, lse, t, h, d, s, stride, topk, sm, dt, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=ps.F32), ps.E_UNSUPPORTED),
+    (dict(dt=9), ps.E_INVAL),
+    (dict(d=256), ps.E_UNSUPPORTED),
+    (dict(h=48), ps.E_UNSUPPORTED),
+    (dict(h=16), ps.E_UNSUPPORTED),
+    (dict(topk=2049), ps.E_UNSUPPORTED),
+    (dict(topk=-1), ps.E_INVAL),
+    (dict(t=-1), ps.E_INVAL),
+    (dict(s=-5), ps.E_INVAL),
+    (dict(stride=500), ps.E_INVAL),
+    (dict(stride=516), ps.E_INVAL),
+    (dict(sm=0.0), ps.E_INVAL),
+    (dict(q=0), ps.E_INVAL),
+    (dict(idx=0), ps.E_INVAL),
+    (dict(ckv=0), ps.E_INVAL),
+    (dict(o=FAKE + 8), ps.E_INVAL),
+    (dict(lse=FAKE + 2), ps.E_INVAL),
+    (dict(sink=FAKE + 1), ps.E_INVAL),
+])
+def test_mla_validation(lib, kw, status):
+    assert _mla(**kw) == status
+    assert ps.psattn_last_error()
+
+
+def test_mla_no_tokens_enqueues_nothing(lib):
+    assert _mla(q=0, ckv=0, idx=0, o=0, lse=0, t=0) == ps.OK
