@@ -11,13 +11,14 @@
 //
 //  * the token's list is staged in LDS and compacted in order (entries
 //    outside [0, num_kv) dropped, one wave ballot per round), so that every
-//    32-key tile but the last is full and needs no mask;
-//  * each tile's 32 latent rows are gathered global -> LDS with
-//    global_load_lds_dwordx4, one 1 KiB row per wave instruction, one tile
-//    ahead in a double buffer.  The chunks of a row land XOR-swizzled by
-//    ((r & 3) << 2) | ((r >> 2) & 3), which keeps both the row reads of the
-//    score product and the transposed reads of the value product free of
-//    bank conflicts: the tile is read both ways, being K and V at once;
+//    16-key tile but the last is full and needs no mask;
+//  * each tile's 16 latent rows are gathered global -> LDS with
+//    global_load_lds_dwordx4, one 1 KiB row per wave instruction, three
+//    tiles ahead in a ring of four buffers.  Row r's chunks land XOR-swizzled
+//    by r & 15; the tile is read both ways (it is K and V at once), as rows
+//    by the score product and transposed by the value product, and the key
+//    order of the value product (key_of) keeps the transposed reads free of
+//    bank conflicts too;
 //  * H / 16 waves.  Scores: wave w takes heads 16 w .. 16 w + 15 (their Q^T
 //    fragments stay in registers), S^T = C Q^T on v_mfma_f32_16x16x32_bf16,
 //    online softmax in the log2 domain with a lazily moved reference maximum;
@@ -41,15 +42,28 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 #define PM_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
-constexpr int kBN = 32;                    // keys per tile
+constexpr int kBN = 16;                    // keys per tile
+constexpr int kNBuf = 4;                   // tile buffers: tiles are gathered kNBuf - 1 ahead
+static_assert(kNBuf >= 2 && kNBuf <= 4, "waits cover up to two tiles in flight");
 constexpr int kRowB = 2 * kMlaDim;         // bytes of a latent row (1 KiB)
-constexpr int kTile = kBN * kRowB;         // 32 KiB
+constexpr int kTile = kBN * kRowB;         // 16 KiB
 constexpr int kNStep = kMlaDim / 32;       // k-steps of the score product (16x16x32)
-constexpr int kPRow = 72;                  // bytes per head row of P in LDS (32 keys, padded)
+constexpr int kPRow = 2 * kBN + 8;         // bytes per head row of P in LDS (padded)
 constexpr float kTau = 8.0f;               // lazy rescale threshold (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ int fsw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Chunk swizzle of tile row r: chunk c of the row sits at c ^ (r & 15).
+__device__ __forceinline__ int fsw(int r) { return r & 15; }
+
+// Key order of the value product inside a 16-key block.  Position
+// i = 8 g + 4 u + e of its contraction (and of P in LDS) is key
+// 4 e + 2 u + g: the four rows that one transposed read gathers (e = 0..3)
+// then differ in bits 2..3, which keeps those reads free of bank conflicts
+// under the swizzle above.  (The score product reads its rows in key order,
+// lane i row i, the one order measured free of conflicts for its 16-byte row
+// reads; its results are scattered to their positions when P is stored.)
+__device__ __forceinline__ int key_of(int i) { return 4 * (i & 3) + 2 * ((i >> 2) & 1) + (i >> 3); }
+__device__ __forceinline__ int pos_of(int k) { return (k >> 2) + 4 * ((k >> 1) & 1) + 8 * (k & 1); }
 
 // NW = H / 16 waves.  Wave w: score heads 16 w .. +15; value dims
 // DW w .. DW (w + 1) with DW = 512 / NW, for head blocks 0 .. HB - 1.
@@ -63,7 +77,7 @@ void mla_sparse_kernel(MlaArgs a) {
   constexpr int PER = kMlaMaxTopk / NT;    // list entries per thread
   constexpr int RPW = kBN / NW;            // tile rows gathered per wave
   static_assert(HB * NDBW == 8, "eight accumulator blocks per wave");
-  __shared__ __attribute__((aligned(1024))) char smem[2][kTile];
+  __shared__ __attribute__((aligned(1024))) char smem[kNBuf][kTile];
   __shared__ __attribute__((aligned(16))) int sidx[kMlaMaxTopk];
   __shared__ __attribute__((aligned(16))) char sp_[H * kPRow];  // P [head][32 keys] bf16
   __shared__ float salpha[H];              // per-head rescale of this tile; 1/l at the end
@@ -135,13 +149,7 @@ void mla_sparse_kernel(MlaArgs a) {
     const int k0 = n * kBN + wave * RPW;
     int ids[RPW];
 #pragma unroll
-    for (int j = 0; j < RPW / 4; ++j) {
-      const i32x4_t v = *reinterpret_cast<const i32x4_t*>(&sidx[k0 + 4 * j]);
-      ids[4 * j] = v[0];
-      ids[4 * j + 1] = v[1];
-      ids[4 * j + 2] = v[2];
-      ids[4 * j + 3] = v[3];
-    }
+    for (int i = 0; i < RPW; ++i) ids[i] = sidx[k0 + i];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = wave * RPW + i;
@@ -163,12 +171,13 @@ void mla_sparse_kernel(MlaArgs a) {
   const float c = a.scale_log2;
 
   // ---- scores of tile kt for this wave's heads -> P and rescale factors in
-  // LDS.  Lane (l16, g4), register e of block kb holds key 16 kb + 4 g4 + e.
+  // LDS.  Lane (l16, g4), register e of block kb holds key 16 kb + 4 g4 + e;
+  // P is stored by position (pos_of).
   auto scores = [&](const char* kt, int nvalid, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
-    f32x4_t sc[2];
+    f32x4_t sc[kBN / 16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kBN / 16; ++kb) {
       sc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int row = 16 * kb + l16;
       const char* krow = kt + row * kRowB;
@@ -181,7 +190,7 @@ void mla_sparse_kernel(MlaArgs a) {
     }
     float mr = -__builtin_inff();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kBN / 16; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (MASK) {
@@ -200,25 +209,26 @@ void mla_sparse_kernel(MlaArgs a) {
     }
     float psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < kBN / 16; ++kb) {
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         p[e] = fast_exp2(__builtin_fmaf(sc[kb][e], c, -m_run));
         psum += p[e];
       }
-      const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      *reinterpret_cast<u32x2_t*>(&sp_[shead * kPRow + 2 * (16 * kb + 4 * g4)]) = pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<__bf16*>(&sp_[shead * kPRow + 2 * (16 * kb + pos_of(4 * g4 + e))]) = (__bf16)p[e];
     }
     l_run += psum;
     if (g4 == 0) salpha[shead] = al;
     if (lane == 0) smoved[wave] = __builtin_amdgcn_ballot_w64(grow) != 0;
   };
 
-  // ---- O^T += C^T P^T for this wave's dims.  The contraction follows the
-  // score layout: position 8 g + e of 16-key step ks is key
-  // 16 ks + 8 (e / 4) + 4 g + e % 4, for the A operand (rows of the tile,
-  // read transposed) and the B operand (P rows) alike.
+  // ---- O^T += C^T P^T for this wave's dims.  Position 8 g + 4 u + e of
+  // 16-key step ks is key 16 ks + key_of(8 g + 4 u + e), for the A operand
+  // (rows of the tile, read transposed: source lane ap + 4 e of a 16-lane
+  // group addresses that row) and the B operand (P, stored by position).
   auto values = [&](const char* kt) __attribute__((always_inline)) {
     int moved = 0;
 #pragma unroll
@@ -240,9 +250,9 @@ void mla_sparse_kernel(MlaArgs a) {
       bf16x8_t pb[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const char* prow = &sp_[(32 * hb + l32) * kPRow + 2 * (16 * ks + 4 * g)];
+        const char* prow = &sp_[(32 * hb + l32) * kPRow + 2 * (16 * ks + 8 * g)];
         const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 16);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
         const u32x4_t both = {lo[0], lo[1], hi[0], hi[1]};
         pb[hb] = __builtin_bit_cast(bf16x8_t, both);
       }
@@ -251,7 +261,7 @@ void mla_sparse_kernel(MlaArgs a) {
         s16x4_t vv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int row = 16 * ks + 8 * u + 4 * g + sp;
+          const int row = 16 * ks + key_of(8 * g + 4 * u + sp);
           const int chunk = 4 * (NDBW * wave + db) + 2 * hgrp + (ap >> 1);
           vv[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               PM_LDS_PTR(s16x4_t, kt + row * kRowB + 16 * (chunk ^ fsw(row)) + 8 * (ap & 1)));
@@ -269,18 +279,30 @@ void mla_sparse_kernel(MlaArgs a) {
   // with explicit vmcnt counts that the compiler does not know about
 #pragma unroll
   for (int s = 0; s < kNStep; ++s) asm volatile("" ::"v"(qf[s]));
-  if (ntile > 0) issue(0, 0);
-  wait_vmcnt<0>();
+  // wait until tile m has landed, when the tiles up to `last` are issued
+  // (copies complete in issue order, RPW per tile and wave)
+  auto wait_tile = [&](int m, int last) __attribute__((always_inline)) {
+    const int later = last - m;
+    if (later <= 0) wait_vmcnt<0>();
+    else if (kNBuf > 2 && later == 1) wait_vmcnt<RPW>();
+    else wait_vmcnt<2 * RPW>();
+  };
+#pragma unroll
+  for (int p = 0; p < kNBuf - 1; ++p)
+    if (p < ntile) issue(p, p);
+  wait_tile(0, (ntile < kNBuf - 1 ? ntile : kNBuf - 1) - 1);
   __syncthreads();
   for (int n = 0; n < ntile; ++n) {
-    if (n + 1 < ntile) issue(n + 1, (n + 1) & 1);
+    const int nx = n + kNBuf - 1;
+    if (nx < ntile) issue(nx, nx % kNBuf);
+    const char* kt = smem[n % kNBuf];
     if (n < nfull)
-      scores(smem[n & 1], kBN, std::false_type{});
+      scores(kt, kBN, std::false_type{});
     else
-      scores(smem[n & 1], cnt - n * kBN, std::true_type{});
+      scores(kt, cnt - n * kBN, std::true_type{});
     __syncthreads();
-    values(smem[n & 1]);
-    wait_vmcnt<0>();
+    values(kt);
+    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
     __syncthreads();
   }
 
