@@ -79,9 +79,11 @@ void mla_sparse_kernel(MlaArgs a) {
   static_assert(HB * NDBW == 8, "eight accumulator blocks per wave");
   __shared__ __attribute__((aligned(1024))) char smem[kNBuf][kTile];
   __shared__ __attribute__((aligned(16))) int sidx[kMlaMaxTopk];
-  __shared__ __attribute__((aligned(16))) char sp_[H * kPRow];  // P [head][32 keys] bf16
-  __shared__ float salpha[H];              // per-head rescale of this tile; 1/l at the end
-  __shared__ int smoved[NW];
+  // P [head][position] bf16, the heads' rescale factors (1 / l at the end) and
+  // the waves' "some head moved" flags, double-buffered by tile parity
+  __shared__ __attribute__((aligned(16))) char sp_[2][H * kPRow];
+  __shared__ float salpha[2][H];
+  __shared__ int smoved[2][NW];
   __shared__ int wcnt[NW];
 
   // later tokens list more keys (a causal prefill): they start first
@@ -173,7 +175,7 @@ void mla_sparse_kernel(MlaArgs a) {
   // ---- scores of tile kt for this wave's heads -> P and rescale factors in
   // LDS.  Lane (l16, g4), register e of block kb holds key 16 kb + 4 g4 + e;
   // P is stored by position (pos_of).
-  auto scores = [&](const char* kt, int nvalid, auto maskc) __attribute__((always_inline)) {
+  auto scores = [&](const char* kt, int nvalid, int pb, auto maskc) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(maskc)::value;
     f32x4_t sc[kBN / 16];
 #pragma unroll
@@ -218,25 +220,25 @@ void mla_sparse_kernel(MlaArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        *reinterpret_cast<__bf16*>(&sp_[shead * kPRow + 2 * (16 * kb + pos_of(4 * g4 + e))]) = (__bf16)p[e];
+        *reinterpret_cast<__bf16*>(&sp_[pb][shead * kPRow + 2 * (16 * kb + pos_of(4 * g4 + e))]) = (__bf16)p[e];
     }
     l_run += psum;
-    if (g4 == 0) salpha[shead] = al;
-    if (lane == 0) smoved[wave] = __builtin_amdgcn_ballot_w64(grow) != 0;
+    if (g4 == 0) salpha[pb][shead] = al;
+    if (lane == 0) smoved[pb][wave] = __builtin_amdgcn_ballot_w64(grow) != 0;
   };
 
   // ---- O^T += C^T P^T for this wave's dims.  Position 8 g + 4 u + e of
   // 16-key step ks is key 16 ks + key_of(8 g + 4 u + e), for the A operand
   // (rows of the tile, read transposed: source lane ap + 4 e of a 16-lane
   // group addresses that row) and the B operand (P, stored by position).
-  auto values = [&](const char* kt) __attribute__((always_inline)) {
+  auto values = [&](const char* kt, int par) __attribute__((always_inline)) {
     int moved = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) moved |= smoved[w];
+    for (int w = 0; w < NW; ++w) moved |= smoved[par][w];
     if (moved) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const float al = salpha[32 * hb + l32];
+        const float al = salpha[par][32 * hb + l32];
 #pragma unroll
         for (int db = 0; db < NDBW; ++db) o[db][hb] *= al;
       }
@@ -250,7 +252,7 @@ void mla_sparse_kernel(MlaArgs a) {
       bf16x8_t pb[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const char* prow = &sp_[(32 * hb + l32) * kPRow + 2 * (16 * ks + 8 * g)];
+        const char* prow = &sp_[par][(32 * hb + l32) * kPRow + 2 * (16 * ks + 8 * g)];
         const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(prow);
         const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(prow + 8);
         const u32x4_t both = {lo[0], lo[1], hi[0], hi[1]};
@@ -287,22 +289,32 @@ void mla_sparse_kernel(MlaArgs a) {
     else if (kNBuf > 2 && later == 1) wait_vmcnt<RPW>();
     else wait_vmcnt<2 * RPW>();
   };
+  // One barrier per tile: iteration n runs the values of tile n (its P was
+  // left by the previous iteration) and then the scores of tile n + 1, whose
+  // rows every wave awaited before that barrier; P, the rescale factors and
+  // the flags alternate between two buffers.
+  auto score_tile = [&](int m) __attribute__((always_inline)) {
+    const char* kt = smem[m % kNBuf];
+    if (m < nfull)
+      scores(kt, kBN, m & 1, std::false_type{});
+    else
+      scores(kt, cnt - m * kBN, m & 1, std::true_type{});
+  };
+  const int lastp = (ntile < kNBuf - 1 ? ntile : kNBuf - 1) - 1;  // tiles issued up front
 #pragma unroll
   for (int p = 0; p < kNBuf - 1; ++p)
     if (p < ntile) issue(p, p);
-  wait_tile(0, (ntile < kNBuf - 1 ? ntile : kNBuf - 1) - 1);
+  wait_tile(0, lastp);
+  __syncthreads();
+  if (ntile > 0) score_tile(0);
+  wait_tile(1, lastp);
   __syncthreads();
   for (int n = 0; n < ntile; ++n) {
     const int nx = n + kNBuf - 1;
     if (nx < ntile) issue(nx, nx % kNBuf);
-    const char* kt = smem[n % kNBuf];
-    if (n < nfull)
-      scores(kt, kBN, std::false_type{});
-    else
-      scores(kt, cnt - n * kBN, std::true_type{});
-    __syncthreads();
-    values(kt);
-    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
+    values(smem[n % kNBuf], n & 1);
+    if (n + 1 < ntile) score_tile(n + 1);
+    wait_tile(n + 2, nx < ntile - 1 ? nx : ntile - 1);
     __syncthreads();
   }
 
@@ -318,7 +330,7 @@ void mla_sparse_kernel(MlaArgs a) {
       den = __builtin_fmaf(lt, so, fast_exp2(s2 - mf));
     }
     if (g4 == 0) {
-      salpha[shead] = den > 0.f ? so / den : 0.f;
+      salpha[0][shead] = den > 0.f ? so / den : 0.f;
       a.lse[(size_t)t * H + shead] = den > 0.f ? (mf + fast_log2(den)) * kLn2 : -__builtin_inff();
     }
   }
@@ -326,7 +338,7 @@ void mla_sparse_kernel(MlaArgs a) {
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = 32 * hb + l32;
-    const float inv = salpha[head];
+    const float inv = salpha[0][head];
     __bf16* op = reinterpret_cast<__bf16*>(a.o) + ((size_t)t * H + head) * kMlaDim;
 #pragma unroll
     for (int db = 0; db < NDBW; ++db) {
