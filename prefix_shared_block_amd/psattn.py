@@ -292,6 +292,12 @@ def fwd_mla(q, ckv, indices, sm_scale: Optional[float] = None, sink=None, out=No
         raise ValueError("ckv must be [S, stride] with unit column stride")
     if indices.dim() != 2 or indices.shape[0] != t_n or not indices.is_contiguous():
         raise ValueError("indices must be a contiguous [T, topk] tensor")
+    if indices.dtype != torch.int32:
+        raise TypeError(f"indices must be int32, not {indices.dtype}")
+    if not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, H, D] tensor")
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != hq or not sink.is_contiguous()):
+        raise ValueError("sink must be a contiguous float32 tensor of H entries")
     if out is None:
         out = torch.empty_like(q)
     if lse is None:

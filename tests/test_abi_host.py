@@ -314,3 +314,17 @@ def test_mla_validation(lib, kw, status):
 
 def test_mla_no_tokens_enqueues_nothing(lib):
     assert _mla(q=0, ckv=0, idx=0, o=0, lse=0, t=0) == ps.OK
+
+
+def test_mla_binding_checks_argument_types(lib):
+    # the binding refuses malformed tensors before any device work
+    import torch
+
+    q = torch.zeros(4, 32, 512, dtype=torch.bfloat16)
+    ckv = torch.zeros(10, 512, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        ps.fwd_mla(q, ckv, torch.zeros(4, 8, dtype=torch.int64))
+    with pytest.raises(ValueError):
+        ps.fwd_mla(q, ckv, torch.zeros(3, 8, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        ps.fwd_mla(q, ckv, torch.zeros(4, 8, dtype=torch.int32), sink=torch.zeros(31))
