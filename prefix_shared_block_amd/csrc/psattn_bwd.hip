@@ -15,7 +15,8 @@
 //      dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T  (dQ = sm_scale dQ^T^T);
 //  * bwd_dkdv: a tile of 128 keys of one kv head per workgroup (32 per wave,
 //    their K^T and V^T fragments in registers) against one chunk of the query
-//    rows that see them, streamed as tiles of 64 stacked rows:
+//    rows that see them, streamed as tiles of 64 stacked rows (copied
+//    global -> LDS three tiles ahead in a ring of four buffers):
 //      S = Q K^T,  P = exp2(S c - lse2),  dP = dO V^T,  dS = P (dP - delta),
 //      dV^T += dO^T P,  dK^T += Q^T dS;
 //    each item adds its partial dK / dV into the fp32 accumulators (a prefix
@@ -311,8 +312,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TILE = RT * C::ROWB;      // Q (or dO) tile bytes
   constexpr int NCOPY = TILE / 1024;      // 1 KiB copies per Q (or dO) tile
   constexpr int CPW = 2 * NCOPY / kWaves; // copies per wave per tile
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float rowv[2][2][RT];     // [buffer][lse2, delta]
+  constexpr int NBUF = 4;                                        // tile ring (NBUF - 1 tiles ahead)
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float rowv[NBUF][2][RT];     // [buffer][lse2, delta]
   __shared__ __attribute__((aligned(16))) int tokoff[RT];           // token offset of stacked row s
 
   const int blk = blockIdx.x;
@@ -511,22 +513,38 @@ void bwd_dkdv_kernel(BwdArgs a) {
     math(bsel, t0, nv, maskc);
   };
 
-  if (ntile > 0) issue(0, 0);
+  // copies complete in issue order: CPW per tile and wave, plus the row
+  // values for waves 0 and 1
+  auto wait_tile = [&](int m, int last) __attribute__((always_inline)) {
+    const int later = last - m;
+    if (later <= 0) wait_vmcnt<0>();
+    else if (wave < 2) {
+      if (later == 1) wait_vmcnt<CPW + 1>(); else wait_vmcnt<2 * (CPW + 1)>();
+    } else {
+      if (later == 1) wait_vmcnt<CPW>(); else wait_vmcnt<2 * CPW>();
+    }
+  };
+  const int lastp = (ntile < NBUF - 1 ? ntile : NBUF - 1) - 1;
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < ntile) issue(p, p);
 #pragma unroll
   for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
-  wait_vmcnt<0>();
+  wait_tile(0, lastp);
   __syncthreads();
   int n = 0;
   for (; n < nmask; ++n) {
-    if (n + 1 < ntile) issue(n + 1, (n + 1) & 1);
-    compute(n, n & 1, std::true_type{});
-    wait_vmcnt<0>();
+    const int nx = n + NBUF - 1;
+    if (nx < ntile) issue(nx, nx % NBUF);
+    compute(n, n % NBUF, std::true_type{});
+    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
     __syncthreads();
   }
   for (; n < ntile; ++n) {
-    if (n + 1 < ntile) issue(n + 1, (n + 1) & 1);
-    compute(n, n & 1, std::false_type{});
-    wait_vmcnt<0>();
+    const int nx = n + NBUF - 1;
+    if (nx < ntile) issue(nx, nx % NBUF);
+    compute(n, n % NBUF, std::false_type{});
+    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
     __syncthreads();
   }
 
@@ -534,7 +552,7 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
   // c ^ kr), then adds it with consecutive lanes on consecutive floats.
   constexpr int SROW = D * 4;
-  static_assert(kWaves * 32 * SROW <= 2 * 2 * TILE, "staging fits in the tiles");
+  static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
   char* st = &smem[0][0][0] + wave * (32 * SROW);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
