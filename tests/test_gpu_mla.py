@@ -122,3 +122,18 @@ def test_mla_dsa_fullsize_sampled(gpu_lib):
     tokens = sorted({0, 1, 31, 32, 33, 2046, 2047, 2048, 8191, 16383} |
                     {int(x) for x in rng.integers(0, inst.num_tokens, size=10)})
     _check(gpu_lib, inst, "mla_dsa sampled", tokens=tokens)
+
+
+def test_mla_empty_cache(gpu_lib):
+    # no cached rows: every entry is out of range, every token has no key
+    import torch
+
+    inst = make_mla(16, 64, 512, 8, seed=9, sink=True)
+    q = torch.from_numpy(inst.q.view(np.int16)).view(torch.bfloat16).cuda()
+    ckv = torch.empty((0, 512), dtype=torch.bfloat16, device="cuda")
+    idx = torch.from_numpy(inst.indices).cuda()
+    sink = torch.from_numpy(inst.sink.astype(np.float32)).cuda()
+    o, lse = gpu_lib.fwd_mla(q, ckv, idx, sm_scale=inst.sm_scale, sink=sink)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert np.allclose(to_f64(lse), np.broadcast_to(inst.sink.astype(np.float64), (16, 64)), rtol=0, atol=1e-6)
