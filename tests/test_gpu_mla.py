@@ -137,3 +137,17 @@ def test_mla_empty_cache(gpu_lib):
     torch.cuda.synchronize()
     assert torch.all(o == 0)
     assert np.allclose(to_f64(lse), np.broadcast_to(inst.sink.astype(np.float64), (16, 64)), rtol=0, atol=1e-6)
+
+
+def test_mla_zero_length_lists(gpu_lib):
+    # topk = 0: no entries at all; without sinks every row is zero with LSE -inf
+    import torch
+
+    inst = make_mla(12, 32, 512, 4, seed=10)
+    q = torch.from_numpy(inst.q.view(np.int16)).view(torch.bfloat16).cuda()
+    ckv = torch.from_numpy(inst.ckv.view(np.int16)).view(torch.bfloat16).cuda()
+    idx = torch.empty((12, 0), dtype=torch.int32, device="cuda")
+    o, lse = gpu_lib.fwd_mla(q, ckv, idx, sm_scale=inst.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0)
+    assert bool(torch.all(torch.isneginf(lse)))
