@@ -209,9 +209,11 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
                kv_dtype: int = BF16, seed: int = 0, num_pages: Optional[int] = None,
                scales: bool = False, poison_unused: bool = True,
                sm_scale: Optional[float] = None, name: str = "paged",
-               draft_lens: Optional[Sequence[int]] = None) -> PagedInstance:
+               draft_lens: Optional[Sequence[int]] = None, page_size: int = PAGE_SIZE) -> PagedInstance:
     """draft_lens: per-request draft lengths (ragged); draft_len is then taken
-    as their maximum and the draft rows are packed back to back."""
+    as their maximum and the draft rows are packed back to back.  page_size:
+    token slots per page (16 for the named workloads; with 16 the draws are
+    the same as before the argument existed)."""
     rng = _rng(seed)
     prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
     b = int(prefix_lens.shape[0])
@@ -223,7 +225,9 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
         qo[1:] = np.cumsum(dl)
         n_rows = int(qo[-1])
         draft_len = int(dl.max()) if dl.size else 0
-    n_b = (prefix_lens + PAGE_SIZE - 1) // PAGE_SIZE
+    if page_size < 1:
+        raise ValueError("page_size must be >= 1")
+    n_b = (prefix_lens + page_size - 1) // page_size
     used = int(n_b.sum())
     if num_pages is None:
         num_pages = max(used, 1)
@@ -231,8 +235,8 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
         raise ValueError("pool too small")
     q = _normal(rng, (n_rows, hq, d))
     # prefix K/V drawn per used page (unused pages are poisoned), then placed
-    kp = _normal(rng, (used, PAGE_SIZE, hkv, d))
-    vp = _normal(rng, (used, PAGE_SIZE, hkv, d))
+    kp = _normal(rng, (used, page_size, hkv, d))
+    vp = _normal(rng, (used, page_size, hkv, d))
     perm = rng.permutation(num_pages).astype(np.int64)
     kx = _normal(rng, (n_rows, hkv, d))
     vx = _normal(rng, (n_rows, hkv, d))
@@ -246,7 +250,7 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
     indices = perm[:used]
     sdt = np.float32 if kv_dtype == F32 else (np.uint16 if kv_dtype == BF16 else np.uint8)
     nan = {F32: np.float32(np.nan), BF16: BF16_NAN, FP8: FP8_NAN}[kv_dtype]
-    shape = (num_pages, PAGE_SIZE, hkv, d)
+    shape = (num_pages, page_size, hkv, d)
     if poison_unused:
         k_pool = np.full(shape, nan, dtype=sdt)
         v_pool = np.full(shape, nan, dtype=sdt)
@@ -258,7 +262,7 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
     if poison_unused:
         # slots past the end of a request's last, partial page are never read
         for bi in range(b):
-            tail = int(prefix_lens[bi] % PAGE_SIZE)
+            tail = int(prefix_lens[bi] % page_size)
             if tail and n_b[bi] > 0:
                 last = indices[indptr[bi + 1] - 1]
                 k_pool[last, tail:] = nan
@@ -271,7 +275,7 @@ def make_paged(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d:
         v_ext=_encode(vx, kv_dtype), draft_len=int(draft_len), hq=hq, hkv=hkv, d=d,
         q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
         sm_scale=float(sm_scale if sm_scale is not None else 1.0 / math.sqrt(d)), seed=seed,
-        qo_indptr=None if qo is None else qo.astype(np.int32))
+        page_size=int(page_size), qo_indptr=None if qo is None else qo.astype(np.int32))
 
 
 # ---------------------------------------------------------------------------
@@ -300,17 +304,18 @@ def make_flat_spikes(prefix_len: int, seg_lens: Sequence[int], hq: int, hkv: int
 
 def make_paged_spikes(prefix_lens: Sequence[int], draft_len: int, hq: int, hkv: int, d: int,
                       spikes: Sequence[int], kv_dtype: int = BF16, seed: int = 0,
-                      num_pages: Optional[int] = None, name: str = "paged_spikes") -> PagedInstance:
+                      num_pages: Optional[int] = None, name: str = "paged_spikes",
+                      page_size: int = PAGE_SIZE) -> PagedInstance:
     """Spikes at the given prefix positions of every request that has them."""
     inst = make_paged(prefix_lens, draft_len, hq, hkv, d, kv_dtype=kv_dtype, seed=seed,
-                      num_pages=num_pages, scales=(kv_dtype == FP8), name=name)
+                      num_pages=num_pages, scales=(kv_dtype == FP8), name=name, page_size=page_size)
     inst.q = _abs_bits(inst.q, inst.q_dtype)
     row = _encode(np.full((hkv, d), 16.0, np.float32), kv_dtype)
     for b, pl in enumerate(inst.prefix_lens):
         for t in spikes:
             if t < pl:
-                page = inst.kv_indices[inst.kv_indptr[b] + t // PAGE_SIZE]
-                inst.k_pool[page, t % PAGE_SIZE] = row
+                page = inst.kv_indices[inst.kv_indptr[b] + t // inst.page_size]
+                inst.k_pool[page, t % inst.page_size] = row
     return inst
 
 

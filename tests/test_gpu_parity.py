@@ -34,7 +34,7 @@ def _paged_check(lib, inst, label=""):
     ro, rl = attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr, inst.kv_indices,
                         inst.prefix_lens, inst.k_ext, inst.v_ext, inst.draft_len, inst.sm_scale,
                         k_scale=inst.k_scale, v_scale=inst.v_scale, q_dtype=inst.q_dtype,
-                        kv_dtype=inst.kv_dtype)
+                        kv_dtype=inst.kv_dtype, page_size=inst.page_size)
     return compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype), label or inst.name)
 
 
@@ -225,7 +225,7 @@ def test_verify_workspace_reused_across_calls(gpu_lib):
         ro, rl = attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr, inst.kv_indices,
                             inst.prefix_lens, inst.k_ext, inst.v_ext, inst.draft_len, inst.sm_scale,
                             k_scale=inst.k_scale, v_scale=inst.v_scale, q_dtype=inst.q_dtype,
-                            kv_dtype=inst.kv_dtype)
+                            kv_dtype=inst.kv_dtype, page_size=inst.page_size)
         compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype),
                 f"reused workspace {list(inst.prefix_lens)[:4]} Lx={inst.draft_len} D={inst.d}")
 

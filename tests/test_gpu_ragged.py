@@ -30,7 +30,7 @@ def test_verify_ragged_draft_lengths(gpu_lib, prefix_lens, lens, hq, hkv, d, kvd
     assert o.shape[0] == sum(lens)
     ro, rl = attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr, inst.kv_indices, inst.prefix_lens,
                         inst.k_ext, inst.v_ext, inst.draft_len, inst.sm_scale, k_scale=inst.k_scale,
-                        v_scale=inst.v_scale, q_dtype=inst.q_dtype, kv_dtype=inst.kv_dtype, draft_mask=mask,
+                        v_scale=inst.v_scale, q_dtype=inst.q_dtype, kv_dtype=inst.kv_dtype, draft_mask=mask, page_size=inst.page_size,
                         qo_indptr=inst.qo_indptr)
     compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype),
             f"ragged {prefix_lens} lens={lens} {hq}/{hkv} D={d} tree={tree}")

@@ -17,7 +17,7 @@ def _tree_check(lib, inst, mask, label):
     o, lse = run_paged(lib, inst, draft_mask=mask)
     ro, rl = attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr, inst.kv_indices, inst.prefix_lens,
                         inst.k_ext, inst.v_ext, inst.draft_len, inst.sm_scale, k_scale=inst.k_scale,
-                        v_scale=inst.v_scale, q_dtype=inst.q_dtype, kv_dtype=inst.kv_dtype, draft_mask=mask)
+                        v_scale=inst.v_scale, q_dtype=inst.q_dtype, kv_dtype=inst.kv_dtype, draft_mask=mask, page_size=inst.page_size)
     return compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype), label)
 
 
