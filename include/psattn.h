@@ -73,8 +73,11 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *     prefix_len, seg_offsets[num_segments] = total_tokens, non-decreasing.
  *     Empty segments are allowed.  num_segments = 0 means the buffer holds the
  *     prefix alone (then total_tokens == prefix_len and seg_offsets may be NULL).
- *   max_seg_len (host): an upper bound of every segment length; it is only
- *     used for validation of sizes, never for correctness.
+ *   max_seg_len (host): a bound of the segment lengths, checked on the host
+ *     only as num_segments * max_seg_len >= total_tokens - prefix_len.  The
+ *     forward does not use it; the backward sizes its dK/dV launch from it,
+ *     and a value below the true longest segment costs time there (the
+ *     workgroups walk the surplus items), never correctness.
  *   seg_parent (device, int32, num_segments entries) or NULL: multi-level
  *     sharing (the multi-level tree "chain" case that the PrefixSharing PR #50
  *     page lists beside the flat GRPO case in its mask-construction section,
@@ -90,11 +93,15 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *     those rows are then wrong).  NULL: one level (every parent is -1).
  *     bf16 only, forward only; ignored in paged mode.
  *
- * Paged mode (speculative target-verify, uniform draft length):
+ * Paged mode (speculative target-verify; draft_len rows per request, or
+ * ragged lengths through qo_indptr):
  *   q, o      [batch * draft_len, Hq, D]; draft row t of request b is row
  *             b * draft_len + t and sits at position prefix_lens[b] + t.
  *   lse       [batch * draft_len, Hq]   fp32
- *   k, v      page pools [num_pages, page_size, Hkv, D] in kv dtype
+ *   k, v      page pools [num_pages, page_size, Hkv, D] in kv dtype; any
+ *             page_size >= 1 (the sglang PR #27382 report, "关键源码片段",
+ *             addresses its k_buffer / v_buffer through kv_indptr / kv_indices
+ *             without fixing a page size)
  *   kv_indptr (device, int32, batch + 1): request b owns the page ids
  *             kv_indices[kv_indptr[b] .. kv_indptr[b+1]); prefix token t of b
  *             is slot t % page_size of page kv_indices[kv_indptr[b] + t / page_size].
@@ -176,8 +183,15 @@ enum {
 
 /*
  * Bytes of scratch the forward call needs for this descriptor (0 in flat
- * mode; paged mode: per-split partial O and LSE in fp32).  Host only; does
- * not touch the GPU.  Returns 0 and sets the last error on invalid input.
+ * mode; paged mode: per-split partial O and LSE in fp32, the first stage's
+ * output that the second stage merges, sglang PR #27382 report, "实现拆解").
+ * The caller owns this memory and passes it to every call, so the library
+ * keeps no buffer of its own between calls (that report's review section,
+ * "评论区精华", describes split scratch buffers cached under the batch size,
+ * one allocation per batch size seen, which bloated device memory).  The
+ * size is a pure function of the descriptor's host fields and the shapes.
+ * Host only; does not touch the GPU.  Returns 0 and sets the last error on
+ * invalid input.
  */
 size_t psattn_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
                              psattn_dtype q_dtype, psattn_dtype kv_dtype);
@@ -229,7 +243,9 @@ size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hk
  *   sm_scale     : the forward's logit scale.
  *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,
  *                  256-byte aligned; its contents on entry do not matter.
- * Enqueues four launches on `stream` (row terms, dQ, dK/dV, conversion).
+ * Enqueues five launches on `stream` (row terms, dQ, dK/dV over the items
+ * that max_seg_len predicts, dK/dV over any items past that bound, and the
+ * conversion).
  * dK and dV sum fp32 partials with atomic adds, so their last bits may
  * differ between calls; dQ is deterministic.  Other configurations return
  * PSATTN_E_UNSUPPORTED with nothing enqueued.
@@ -272,7 +288,9 @@ psattn_status psattn_mla_fwd(const void* q, const void* ckv, const int32_t* indi
 
 /*
  * Test hook: run the segment planner ON THE DEVICE for every workgroup of the
- * prefix-pass launch psattn_fwd would make and write its work items
+ * prefix-pass launch psattn_fwd would make and write its work items (the
+ * PrefixSharing PR #50 page, "设计简介", proposes describing the visibility
+ * by rectangles instead of a dense mask; the items are those rectangles)
  * (PSATTN_ITEM_FIELDS int32 each, in workgroup order) to items_dev, which
  * must hold `capacity` items.  info_host (host) receives the plan summary.
  * With items_dev == NULL only info_host is filled (no GPU work).

@@ -301,12 +301,22 @@ void bwd_dq_kernel(BwdArgs a) {
 }
 
 // --------------------------------------------------------------- dK/dV pass
-template <int D>
 // One wave per SIMD: the fixed K^T / V^T fragments (64 VGPRs) and the two
 // accumulators (128) leave too little of a 256-register budget; at two waves
 // per SIMD the spills cost more than the second wave gains.
+//
+// The workgroup takes item first_item + blockIdx / Hkv of its kv head.
+// WALK = true: it then walks on with a stride of the grid's workgroups per kv
+// head, until the first item past the end (items are numbered without
+// gaps).  The host sizes the one-item launch (WALK = false) from its bound on
+// the rollout lengths and adds a small walking launch from the first item
+// past that bound, so the result never depends on the bound.  (For WALK =
+// false the loop below ends after its first pass and compiles to the
+// straight-line kernel; a loop taken by every workgroup changed the schedule
+// of the tile loop and cost about 9% per call.)
+template <int D, bool WALK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void bwd_dkdv_kernel(BwdArgs a) {
+void bwd_dkdv_kernel(BwdArgs a, int first_item) {
   using C = BCfg<D>;
   constexpr int RT = 64;                  // stacked query rows per tile
   constexpr int TILE = RT * C::ROWB;      // Q (or dO) tile bytes
@@ -319,266 +329,270 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
   const int blk = blockIdx.x;
   const int h_kv = blk % a.hkv;
-  const BwdItem bi = dkdv_item(blk / a.hkv, a.prefix_len, a.nseg, a.seg_offsets, a.row_chunk);
-  if (!bi.valid) return;
+  const int nper = (int)(gridDim.x / (unsigned)a.hkv);
+  for (int item = first_item + blk / a.hkv;; item += nper) {
+    const BwdItem bi = dkdv_item(item, a.prefix_len, a.nseg, a.seg_offsets, a.row_chunk);
+    if (!bi.valid) return;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-  const int G = a.g;
-  const int TT = RT / G;          // query tokens per tile
-  const int vrows_full = TT * G;  // valid stacked rows of a whole tile
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int G = a.g;
+    const int TT = RT / G;          // query tokens per tile
+    const int vrows_full = TT * G;  // valid stacked rows of a whole tile
 
-  if (tid < RT) tokoff[tid] = tid / G;
+    if (tid < RT) tokoff[tid] = tid / G;
 
-  // this lane's key: column l32 of the wave's 32 keys
-  const int key = bi.k0 + 32 * wave + l32;
-  const bool kvalid = key < bi.k1;
-  const int key_c = kvalid ? key : bi.k1 - 1;
-  // K^T and V^T fragments (B operands): k-step s, lane group g holds
-  // d = 16 s + 8 g .. +8 of this lane's key
-  bf16x8_t kf[C::NSTEP], vf[C::NSTEP];
-  {
-    const size_t krow = ((size_t)key_c * a.hkv + h_kv) * D;
-    const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + krow;
-    const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + krow;
-#pragma unroll
-    for (int s = 0; s < C::NSTEP; ++s) {
-      kf[s] = *reinterpret_cast<const bf16x8_t*>(kp + 16 * s + 8 * g);
-      vf[s] = *reinterpret_cast<const bf16x8_t*>(vp + 16 * s + 8 * g);
-    }
-  }
-
-  const int ntile = cdiv32(bi.r1 - bi.r0, TT);
-  // masked tiles: those with a row token below the last key (causal), and the
-  // last tile when it is partial (or when G does not divide RT); they run
-  // first, then the clean ones
-  const int kmax = bi.k1 - 1;  // last key of the item
-  int ndiag = kmax > bi.r0 ? cdiv32(kmax - bi.r0, TT) : 0;
-  ndiag = ndiag < ntile ? ndiag : ntile;
-  // when G does not divide RT every tile has unused rows: all are masked
-  const bool all_mask = vrows_full < RT;
-  const bool extra = !all_mask && ((bi.r1 - bi.r0) % TT != 0) && ntile > ndiag;  // partial last tile
-  const int nmask = all_mask ? ntile : ndiag + (extra ? 1 : 0);
-  auto tile_of = [&](int n) __attribute__((always_inline)) {
-    if (all_mask || n < ndiag) return n;
-    if (extra) return n == ndiag ? ntile - 1 : n - 1;
-    return n;
-  };
-
-  // copies: waves 0, 1 copy the Q tile, waves 2, 3 the dO tile; copy t of a
-  // wave is 1 KiB block jb, lane l on stacked row s = 4 jb + l / 16, chunk l % 16
-  const bool w_isd = wave * CPW >= NCOPY;
-  const char* src = reinterpret_cast<const char*>(w_isd ? a.dout : a.q);
-  const uint32_t tok_stride = (uint32_t)a.hq * C::ROWB;
-  uint32_t coff[CPW];
-#pragma unroll
-  for (int t = 0; t < CPW; ++t) {
-    const int jb = (wave * CPW + t) % NCOPY;
-    const int s = jb * 4 + lane / C::CPR;
-    const int pos = lane % C::CPR;
-    const int sc_ = s < vrows_full ? s : vrows_full - 1;
-    coff[t] = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB + 16u * (uint32_t)(pos ^ C::fb(s));
-  }
-  // per-row values: wave 0 copies lse2, wave 1 delta (one dword per lane)
-  const float* rsrc = wave == 0 ? a.lse2 : a.delta;
-  const int s_l = lane < vrows_full ? lane : vrows_full - 1;
-  const uint32_t roff = (uint32_t)((s_l / G) * a.hq + (s_l % G)) * 4u;
-
-  auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
-    const int tl = tile_of(n);
-    const int t0 = bi.r0 + tl * TT;
-    const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;  // valid stacked rows
-    const char* base = src + ((size_t)t0 * a.hq + (size_t)h_kv * G) * C::ROWB;
-    if (nv == RT) {
-#pragma unroll
-      for (int t = 0; t < CPW; ++t) {
-        const int jb = (wave * CPW + t) % NCOPY;
-        dma16_s(base, coff[t], lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < CPW; ++t) {
-        const int jb = (wave * CPW + t) % NCOPY;
-        const int s = jb * 4 + lane / C::CPR;
-        const int pos = lane % C::CPR;
-        const int sc_ = s < nv ? s : nv - 1;
-        const uint32_t off = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB +
-                             16u * (uint32_t)(pos ^ C::fb(s));
-        dma16_s(base, off, lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
+    // this lane's key: column l32 of the wave's 32 keys
+    const int key = bi.k0 + 32 * wave + l32;
+    const bool kvalid = key < bi.k1;
+    const int key_c = kvalid ? key : bi.k1 - 1;
+    // K^T and V^T fragments (B operands): k-step s, lane group g holds
+    // d = 16 s + 8 g .. +8 of this lane's key
+    bf16x8_t kf[C::NSTEP], vf[C::NSTEP];
+    {
+      const size_t krow = ((size_t)key_c * a.hkv + h_kv) * D;
+      const __bf16* kp = reinterpret_cast<const __bf16*>(a.k) + krow;
+      const __bf16* vp = reinterpret_cast<const __bf16*>(a.v) + krow;
+  #pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        kf[s] = *reinterpret_cast<const bf16x8_t*>(kp + 16 * s + 8 * g);
+        vf[s] = *reinterpret_cast<const bf16x8_t*>(vp + 16 * s + 8 * g);
       }
     }
-    if (wave < 2) {
-      const float* rb = rsrc + (size_t)t0 * a.hq + (size_t)h_kv * G;
-      uint32_t ro = roff;
-      if (nv < RT) {
-        const int sl = lane < nv ? lane : nv - 1;
-        ro = (uint32_t)((sl / G) * a.hq + (sl % G)) * 4u;
+
+    const int ntile = cdiv32(bi.r1 - bi.r0, TT);
+    // masked tiles: those with a row token below the last key (causal), and the
+    // last tile when it is partial (or when G does not divide RT); they run
+    // first, then the clean ones
+    const int kmax = bi.k1 - 1;  // last key of the item
+    int ndiag = kmax > bi.r0 ? cdiv32(kmax - bi.r0, TT) : 0;
+    ndiag = ndiag < ntile ? ndiag : ntile;
+    // when G does not divide RT every tile has unused rows: all are masked
+    const bool all_mask = vrows_full < RT;
+    const bool extra = !all_mask && ((bi.r1 - bi.r0) % TT != 0) && ntile > ndiag;  // partial last tile
+    const int nmask = all_mask ? ntile : ndiag + (extra ? 1 : 0);
+    auto tile_of = [&](int n) __attribute__((always_inline)) {
+      if (all_mask || n < ndiag) return n;
+      if (extra) return n == ndiag ? ntile - 1 : n - 1;
+      return n;
+    };
+
+    // copies: waves 0, 1 copy the Q tile, waves 2, 3 the dO tile; copy t of a
+    // wave is 1 KiB block jb, lane l on stacked row s = 4 jb + l / 16, chunk l % 16
+    const bool w_isd = wave * CPW >= NCOPY;
+    const char* src = reinterpret_cast<const char*>(w_isd ? a.dout : a.q);
+    const uint32_t tok_stride = (uint32_t)a.hq * C::ROWB;
+    uint32_t coff[CPW];
+  #pragma unroll
+    for (int t = 0; t < CPW; ++t) {
+      const int jb = (wave * CPW + t) % NCOPY;
+      const int s = jb * 4 + lane / C::CPR;
+      const int pos = lane % C::CPR;
+      const int sc_ = s < vrows_full ? s : vrows_full - 1;
+      coff[t] = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB + 16u * (uint32_t)(pos ^ C::fb(s));
+    }
+    // per-row values: wave 0 copies lse2, wave 1 delta (one dword per lane)
+    const float* rsrc = wave == 0 ? a.lse2 : a.delta;
+    const int s_l = lane < vrows_full ? lane : vrows_full - 1;
+    const uint32_t roff = (uint32_t)((s_l / G) * a.hq + (s_l % G)) * 4u;
+
+    auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
+      const int tl = tile_of(n);
+      const int t0 = bi.r0 + tl * TT;
+      const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;  // valid stacked rows
+      const char* base = src + ((size_t)t0 * a.hq + (size_t)h_kv * G) * C::ROWB;
+      if (nv == RT) {
+  #pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+          const int jb = (wave * CPW + t) % NCOPY;
+          dma16_s(base, coff[t], lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
+        }
+      } else {
+  #pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+          const int jb = (wave * CPW + t) % NCOPY;
+          const int s = jb * 4 + lane / C::CPR;
+          const int pos = lane % C::CPR;
+          const int sc_ = s < nv ? s : nv - 1;
+          const uint32_t off = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB +
+                               16u * (uint32_t)(pos ^ C::fb(s));
+          dma16_s(base, off, lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
+        }
       }
-      dma4_s(rb, ro, lds_addr(&rowv[bsel][wave][0]));
-    }
-  };
+      if (wave < 2) {
+        const float* rb = rsrc + (size_t)t0 * a.hq + (size_t)h_kv * G;
+        uint32_t ro = roff;
+        if (nv < RT) {
+          const int sl = lane < nv ? lane : nv - 1;
+          ro = (uint32_t)((sl / G) * a.hq + (sl % G)) * 4u;
+        }
+        dma4_s(rb, ro, lds_addr(&rowv[bsel][wave][0]));
+      }
+    };
 
-  f32x16_t dk[C::NDB], dv[C::NDB];
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      dk[db][e] = 0.f;
-      dv[db][e] = 0.f;
-    }
-  const float c = a.scale_log2;
-  const int li = lane & 15;
-  const int sp = li >> 2;
-  const int ap = li & 3;
-  const int hgrp = l32 >> 4;
-
-  auto math = [&](int bsel, int t0, int nv, auto maskc) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(maskc)::value;
-    const char* qt = smem[bsel][0];
-    const char* dt = smem[bsel][1];
-    const float* l2 = rowv[bsel][0];
-    const float* dl = rowv[bsel][1];
-#pragma unroll
-    for (int rb = 0; rb < RT / 32; ++rb) {
-      // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
-      f32x16_t sc, dp;
-#pragma unroll
+    f32x16_t dk[C::NDB], dv[C::NDB];
+  #pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+  #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sc[e] = 0.f;
-        dp[e] = 0.f;
+        dk[db][e] = 0.f;
+        dv[db][e] = 0.f;
       }
-      const int row = 32 * rb + l32;
-#pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) {
-        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
-      }
-      bf16x8_t pb[2], db_[2];  // k-step ks (16 rows): regs 8 ks .. 8 ks + 7
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int s0 = 32 * rb + 8 * q4 + 4 * g;  // rows s0 .. s0 + 3 of regs 4 q4 .. 4 q4 + 3
-        const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(l2 + s0);
-        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dl + s0);
-        int4 tv;
-        if constexpr (MASK) tv = *reinterpret_cast<const int4*>(tokoff + s0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * q4 + e;
-          float p = fast_exp2(__builtin_fmaf(sc[i], c, -lv[e]));
-          if constexpr (MASK) {
-            const int te = e == 0 ? tv.x : (e == 1 ? tv.y : (e == 2 ? tv.z : tv.w));
-            const bool vis = (s0 + e < nv) && (key <= t0 + te);
-            p = vis ? p : 0.f;
+    const float c = a.scale_log2;
+    const int li = lane & 15;
+    const int sp = li >> 2;
+    const int ap = li & 3;
+    const int hgrp = l32 >> 4;
+
+    auto math = [&](int bsel, int t0, int nv, auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
+      const char* qt = smem[bsel][0];
+      const char* dt = smem[bsel][1];
+      const float* l2 = rowv[bsel][0];
+      const float* dl = rowv[bsel][1];
+  #pragma unroll
+      for (int rb = 0; rb < RT / 32; ++rb) {
+        // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
+        f32x16_t sc, dp;
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sc[e] = 0.f;
+          dp[e] = 0.f;
+        }
+        const int row = 32 * rb + l32;
+  #pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
+        }
+  #pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
+        }
+        bf16x8_t pb[2], db_[2];  // k-step ks (16 rows): regs 8 ks .. 8 ks + 7
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int s0 = 32 * rb + 8 * q4 + 4 * g;  // rows s0 .. s0 + 3 of regs 4 q4 .. 4 q4 + 3
+          const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(l2 + s0);
+          const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dl + s0);
+          int4 tv;
+          if constexpr (MASK) tv = *reinterpret_cast<const int4*>(tokoff + s0);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q4 + e;
+            float p = fast_exp2(__builtin_fmaf(sc[i], c, -lv[e]));
+            if constexpr (MASK) {
+              const int te = e == 0 ? tv.x : (e == 1 ? tv.y : (e == 2 ? tv.z : tv.w));
+              const bool vis = (s0 + e < nv) && (key <= t0 + te);
+              p = vis ? p : 0.f;
+            }
+            pb[i >> 3][i & 7] = (__bf16)p;
+            db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dv4[e]));
           }
-          pb[i >> 3][i & 7] = (__bf16)p;
-          db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dv4[e]));
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: A operand lane (d, g) = rows
+        // 32 rb + 16 ks + 8 t + 4 g + 0..3 of column d, read transposed
+  #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+  #pragma unroll
+          for (int dbk = 0; dbk < C::NDB; ++dbk) {
+            s16x4_t ov[2], qv[2];
+  #pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
+              const int chunk = 4 * dbk + 2 * hgrp + (ap >> 1);
+              const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
+              ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
+              qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
+            }
+            const s16x8_t o8 = {ov[0][0], ov[0][1], ov[0][2], ov[0][3], ov[1][0], ov[1][1], ov[1][2], ov[1][3]};
+            const s16x8_t q8 = {qv[0][0], qv[0][1], qv[0][2], qv[0][3], qv[1][0], qv[1][1], qv[1][2], qv[1][3]};
+            dv[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, o8), pb[ks], dv[dbk], 0, 0, 0);
+            dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q8), db_[ks], dk[dbk], 0, 0, 0);
+          }
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS: A operand lane (d, g) = rows
-      // 32 rb + 16 ks + 8 t + 4 g + 0..3 of column d, read transposed
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int dbk = 0; dbk < C::NDB; ++dbk) {
-          s16x4_t ov[2], qv[2];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
-            const int chunk = 4 * dbk + 2 * hgrp + (ap >> 1);
-            const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
-            ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
-            qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
-          }
-          const s16x8_t o8 = {ov[0][0], ov[0][1], ov[0][2], ov[0][3], ov[1][0], ov[1][1], ov[1][2], ov[1][3]};
-          const s16x8_t q8 = {qv[0][0], qv[0][1], qv[0][2], qv[0][3], qv[1][0], qv[1][1], qv[1][2], qv[1][3]};
-          dv[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, o8), pb[ks], dv[dbk], 0, 0, 0);
-          dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q8), db_[ks], dk[dbk], 0, 0, 0);
+    };
+
+    auto compute = [&](int n, int bsel, auto maskc) __attribute__((always_inline)) {
+      const int tl = tile_of(n);
+      const int t0 = bi.r0 + tl * TT;
+      const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;
+      math(bsel, t0, nv, maskc);
+    };
+
+    // copies complete in issue order: CPW per tile and wave, plus the row
+    // values for waves 0 and 1
+    auto wait_tile = [&](int m, int last) __attribute__((always_inline)) {
+      const int later = last - m;
+      if (later <= 0) wait_vmcnt<0>();
+      else if (wave < 2) {
+        if (later == 1) wait_vmcnt<CPW + 1>(); else wait_vmcnt<2 * (CPW + 1)>();
+      } else {
+        if (later == 1) wait_vmcnt<CPW>(); else wait_vmcnt<2 * CPW>();
+      }
+    };
+    const int lastp = (ntile < NBUF - 1 ? ntile : NBUF - 1) - 1;
+  #pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p)
+      if (p < ntile) issue(p, p);
+  #pragma unroll
+    for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
+    wait_tile(0, lastp);
+    __syncthreads();
+    int n = 0;
+    for (; n < nmask; ++n) {
+      const int nx = n + NBUF - 1;
+      if (nx < ntile) issue(nx, nx % NBUF);
+      compute(n, n % NBUF, std::true_type{});
+      wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
+      __syncthreads();
+    }
+    for (; n < ntile; ++n) {
+      const int nx = n + NBUF - 1;
+      if (nx < ntile) issue(nx, nx % NBUF);
+      compute(n, n % NBUF, std::false_type{});
+      wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
+      __syncthreads();
+    }
+
+    // Add the item's partial dK^T / dV^T into the fp32 accumulators.  Each wave
+    // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
+    // c ^ kr), then adds it with consecutive lanes on consecutive floats.
+    constexpr int SROW = D * 4;
+    static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
+    char* st = &smem[0][0][0] + wave * (32 * SROW);
+  #pragma unroll
+    for (int which = 0; which < 2; ++which) {
+  #pragma unroll
+      for (int dbk = 0; dbk < C::NDB; ++dbk)
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
+          const f32x4_t x = which == 0 ? f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]}
+                                       : f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
+          *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ l32)) = x;
+        }
+      __syncthreads();
+      float* acc = which == 0 ? a.acc_v : a.acc_k;
+  #pragma unroll 4
+      for (int p = lane; p < 32 * D; p += 64) {
+        const int kr = p / D;
+        const int f = p % D;
+        const int kk = bi.k0 + 32 * wave + kr;
+        if (kk < bi.k1) {
+          const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ kr) + 4 * (f & 3));
+          unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + f, x);
         }
       }
+      __syncthreads();
     }
-  };
-
-  auto compute = [&](int n, int bsel, auto maskc) __attribute__((always_inline)) {
-    const int tl = tile_of(n);
-    const int t0 = bi.r0 + tl * TT;
-    const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;
-    math(bsel, t0, nv, maskc);
-  };
-
-  // copies complete in issue order: CPW per tile and wave, plus the row
-  // values for waves 0 and 1
-  auto wait_tile = [&](int m, int last) __attribute__((always_inline)) {
-    const int later = last - m;
-    if (later <= 0) wait_vmcnt<0>();
-    else if (wave < 2) {
-      if (later == 1) wait_vmcnt<CPW + 1>(); else wait_vmcnt<2 * (CPW + 1)>();
-    } else {
-      if (later == 1) wait_vmcnt<CPW>(); else wait_vmcnt<2 * CPW>();
-    }
-  };
-  const int lastp = (ntile < NBUF - 1 ? ntile : NBUF - 1) - 1;
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < ntile) issue(p, p);
-#pragma unroll
-  for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
-  wait_tile(0, lastp);
-  __syncthreads();
-  int n = 0;
-  for (; n < nmask; ++n) {
-    const int nx = n + NBUF - 1;
-    if (nx < ntile) issue(nx, nx % NBUF);
-    compute(n, n % NBUF, std::true_type{});
-    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
-    __syncthreads();
-  }
-  for (; n < ntile; ++n) {
-    const int nx = n + NBUF - 1;
-    if (nx < ntile) issue(nx, nx % NBUF);
-    compute(n, n % NBUF, std::false_type{});
-    wait_tile(n + 1, nx < ntile - 1 ? nx : ntile - 1);
-    __syncthreads();
-  }
-
-  // Add the item's partial dK^T / dV^T into the fp32 accumulators.  Each wave
-  // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
-  // c ^ kr), then adds it with consecutive lanes on consecutive floats.
-  constexpr int SROW = D * 4;
-  static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
-  char* st = &smem[0][0][0] + wave * (32 * SROW);
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-#pragma unroll
-    for (int dbk = 0; dbk < C::NDB; ++dbk)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
-        const f32x4_t x = which == 0 ? f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]}
-                                     : f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
-        *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ l32)) = x;
-      }
-    __syncthreads();
-    float* acc = which == 0 ? a.acc_v : a.acc_k;
-#pragma unroll 4
-    for (int p = lane; p < 32 * D; p += 64) {
-      const int kr = p / D;
-      const int f = p % D;
-      const int kk = bi.k0 + 32 * wave + kr;
-      if (kk < bi.k1) {
-        const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ kr) + 4 * (f & 3));
-        unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + f, x);
-      }
-    }
-    __syncthreads();
-  }
+    if constexpr (!WALK) return;
+  }  // items
 }
 
 // ------------------------------------------------------- pre and post passes
@@ -631,6 +645,10 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int64_t n8) {
   reinterpret_cast<u32x4_t*>(a.dv)[i] = vo;
 }
 
+// workgroups per kv head of the dK/dV launch that walks the items past the
+// host bound
+constexpr int kBwdWalkPerHead = 4;
+
 template <int D>
 int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipStream_t s) {
   const int64_t nrows = a.total_tokens * a.hq;
@@ -646,7 +664,13 @@ int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipSt
     if ((err = (int)hipGetLastError())) return err;
   }
   if (dkdv_blocks > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)dkdv_blocks), dim3(kThreads), 0, s, a);
+    // the items the host bound predicts, one per workgroup ...
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)dkdv_blocks), dim3(kThreads), 0, s, a, 0);
+    if ((err = (int)hipGetLastError())) return err;
+    // ... and any past it (none when the bound holds: the workgroups then find
+    // their first item past the end and return)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(kBwdWalkPerHead * a.hkv)), dim3(kThreads), 0, s,
+                       a, (int)(dkdv_blocks / a.hkv));
     if ((err = (int)hipGetLastError())) return err;
   }
   const int64_t n8 = a.total_tokens * a.hkv * D / 8;

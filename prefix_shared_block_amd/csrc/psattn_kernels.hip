@@ -722,14 +722,14 @@ static int launch_flat_t(const FlatArgs& a, int64_t n_blocks, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
+// fp32 inputs run flat_fwd_kernel; bf16 runs the LDS-DMA kernel of psattn_flat.hip
 int launch_flat(const FlatArgs& a, int d, int dtype, int64_t n_blocks, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool f32 = dtype == DT_F32;
-  if (!f32) return launch_flat_bf16(a, d, n_blocks, stream);
+  if (dtype != DT_F32) return launch_flat_bf16(a, d, n_blocks, stream);
   switch (d) {
-    case 64: return f32 ? launch_flat_t<64, true>(a, n_blocks, s) : launch_flat_t<64, false>(a, n_blocks, s);
-    case 128: return f32 ? launch_flat_t<128, true>(a, n_blocks, s) : launch_flat_t<128, false>(a, n_blocks, s);
-    case 256: return f32 ? launch_flat_t<256, true>(a, n_blocks, s) : launch_flat_t<256, false>(a, n_blocks, s);
+    case 64: return launch_flat_t<64, true>(a, n_blocks, s);
+    case 128: return launch_flat_t<128, true>(a, n_blocks, s);
+    case 256: return launch_flat_t<256, true>(a, n_blocks, s);
   }
   return (int)hipErrorInvalidValue;
 }

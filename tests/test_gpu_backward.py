@@ -25,14 +25,16 @@ def _dout(inst, seed):
     return f32_to_bf16_bits(rng.standard_normal(inst.q.shape).astype(np.float32))
 
 
-def _run(ps, inst, do_bits, ws_fill=None, repeat=1):
+def _run(ps, inst, do_bits, ws_fill=None, repeat=1, max_seg_len=None):
     import torch
+
+    msl = inst.max_seg_len if max_seg_len is None else max_seg_len
 
     q = to_dev(inst.q, BF16)
     k = to_dev(inst.k, BF16)
     v = to_dev(inst.v, BF16)
     seg = torch.from_numpy(inst.seg_offsets.astype(np.int32)).cuda() if inst.num_segments > 0 else None
-    o, lse = ps.fwd_flat(q, k, v, inst.prefix_len, seg, inst.max_seg_len, sm_scale=inst.sm_scale)
+    o, lse = ps.fwd_flat(q, k, v, inst.prefix_len, seg, msl, sm_scale=inst.sm_scale)
     do = to_dev(do_bits, BF16)
     dq, dqf = guarded_empty(q.shape, torch.bfloat16)
     dk, dkf = guarded_empty(k.shape, torch.bfloat16)
@@ -40,13 +42,12 @@ def _run(ps, inst, do_bits, ws_fill=None, repeat=1):
     ws = None
     if ws_fill is not None:
         n = int(inst.num_segments)
-        desc = ps.flat_desc(inst.total_tokens, inst.prefix_len, n, 0 if seg is None else seg.data_ptr(),
-                            inst.max_seg_len)
+        desc = ps.flat_desc(inst.total_tokens, inst.prefix_len, n, 0 if seg is None else seg.data_ptr(), msl)
         nb = ps.psattn_bwd_workspace_size(desc, inst.hq, inst.hkv, inst.d, BF16)
         ws = torch.full((nb,), ws_fill, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(repeat):
-        ps.bwd_flat(q, k, v, o, lse, do, inst.prefix_len, seg, inst.max_seg_len, sm_scale=inst.sm_scale,
+        ps.bwd_flat(q, k, v, o, lse, do, inst.prefix_len, seg, msl, sm_scale=inst.sm_scale,
                     dq=dq, dk=dk, dv=dv, workspace=ws)
         torch.cuda.synchronize()
         outs.append((dq.clone(), dk.clone(), dv.clone()))
@@ -54,9 +55,9 @@ def _run(ps, inst, do_bits, ws_fill=None, repeat=1):
     return outs
 
 
-def _check(ps, inst, seed=7, label=""):
+def _check(ps, inst, seed=7, label="", max_seg_len=None):
     do_bits = _dout(inst, seed)
-    (dq, dk, dv), = _run(ps, inst, do_bits)
+    (dq, dk, dv), = _run(ps, inst, do_bits, max_seg_len=max_seg_len)
     ref = attn_flat_bwd(inst.q, inst.k, inst.v, do_bits, inst.prefix_len, inst.seg_offsets, inst.sm_scale,
                         dtype=BF16)
     errs = {}
@@ -139,3 +140,16 @@ def test_bwd_workspace_contents_do_not_matter_and_dq_is_deterministic(gpu_lib):
     for j in (1, 2):  # dK, dV sum partials with atomics: equal up to the order of the additions
         x, y = to_f64(a[0][j]), to_f64(b[0][j])
         assert np.max(np.abs(x - y)) <= 1e-2 * max(np.max(np.abs(y)), 1e-30)
+
+
+@pytest.mark.parametrize("p,lens,msl", [
+    (100, [1000, 24], 512),           # passes the host check (2 x 512 >= 1024), true longest 1000
+    (64, [2000, 10, 10, 10], 508),    # 4 x 508 >= 2030, true longest 2000
+])
+def test_bwd_underestimated_max_seg_len(gpu_lib, p, lens, msl):
+    """max_seg_len below the longest rollout still passes the host check
+    (N * max_seg_len >= T - P); the dK/dV launch sized from it walks the
+    surplus items, so the gradients stay exact."""
+    assert len(lens) * msl >= sum(lens) and max(lens) > msl
+    inst = make_flat(p, lens, 8, 2, 128, dtype=BF16, seed=p + sum(lens))
+    _check(gpu_lib, inst, label=f"P={p} lens={lens} max_seg_len={msl}", max_seg_len=msl)
