@@ -1,25 +1,35 @@
 """Benchmark of prefix-shared attention forward on one MI355X.
 
-Headline workload (the step timed K times): the GRPO flat-packed forward,
-P=2048 shared prompt + 8 rollouts x 512 tokens, Hq=32, Hkv=8, D=128, bf16 --
-planner, prefix pass, own-rollout diagonal and epilogue in one launch.
-``value`` is useful TFLOP/s: 4*D*Hq per visible (query row, key) pair,
-masked pairs and softmax excluded.
+Every timed call is one ``psattn_fwd`` over one whole workload: the planner,
+the prefix pass, the own-rollout (or draft) diagonal, the split merge and
+the epilogue, all in the library's kernels.  The default run times all five
+workloads:
 
-In the same run the verify path (paged split-KV pass + log-sum-exp combine)
-is timed on 8 requests x 16384 prefix tokens, Lx=4, Hq=32, Hkv=8, D=128,
-bf16 ("verify us @16k", with its HBM GB/s against the algorithmic bytes that
-count every prefix K/V byte once), and, with --all, the fp8 verify and the
-large ragged GRPO workloads.
+* ``tiny``        P=64 + 2 x 16, Hq=Hkv=2, D=64, fp32 (latency only);
+* ``grpo``        P=2048 + 8 rollouts x 512, Hq=32, Hkv=8, D=128, bf16;
+* ``verify16k``   8 requests x 16384 paged prefix tokens, 4 draft tokens,
+                  Hq=32, Hkv=8, D=128, bf16 ("verify us @16k");
+* ``verify_fp8``  4 x 32768 paged prefix, 8 drafts, Hq=16, Hkv=2, D=256,
+                  fp8 e4m3 K/V with per-tensor scales;
+* ``grpo_ragged`` P=8192 + 16 rollouts of U{256..1024} tokens, Hq=64, Hkv=8,
+                  D=128, bf16, 1% of key rows x8 -- the headline: ``value`` is
+                  its useful TFLOP/s (4 D Hq per visible (query row, key)
+                  pair; masked pairs and the softmax excluded).
 
-Every timed call is preceded (outside the timed events) by a 1 GiB read
-(a reduction over a scratch buffer) that evicts L2 and the 256 MiB MALL, so
-every K/V byte is read from HBM.  A read is used rather than a write so that
-no dirty lines are left to be written back while the timed kernel runs.
-Before timing, each workload's first call is checked for finite outputs.
-Parity with the float64 oracle at these same shapes and launch configurations
-is the GPU test suite's job (the full-size sampled tests); the oracle runs
-here only as the host baseline.
+Each workload reports its time distribution (mean, p10, p50, p90 over the
+timed calls), useful TFLOP/s, HBM GB/s against its algorithmic bytes (every
+K/V byte counted once), and the fraction of the roof that binds it: dense
+bf16 MFMA (2500 TFLOP/s) for the GRPO shapes, HBM (8000 GB/s) for the verify
+shapes.  The GRPO backward is timed too; with --all, the two-level sharing
+and sparse-MLA workloads as well.
+
+Every timed call is preceded (outside its events) by a 1 GiB read that
+evicts L2 and the 256 MiB MALL, so every K/V byte comes from HBM; a read, so
+that no dirty lines are written back during the timed call.  The events are
+recorded on the stream the kernels are launched on.  Before timing, each
+workload's first call is checked for finite outputs; parity with the float64
+oracle at these shapes and launch configurations is the GPU tests' job (the
+full-size tests), and the oracle runs here only as the host baseline.
 """
 from __future__ import annotations
 
@@ -27,6 +37,7 @@ import argparse
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -38,8 +49,10 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "useful TFLOP/s + HBM GB/s (% roofline) of prefix-shared attn fwd; verify µs @16k"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 FLUSH_BYTES = 1 << 30
+HEADLINE = "grpo_ragged"
 
 
 def log(msg):
@@ -55,6 +68,20 @@ def flat_visible_pairs(inst) -> int:
 
 def flat_useful_flops(inst) -> float:
     return 4.0 * inst.d * inst.hq * flat_visible_pairs(inst)
+
+
+def flat_rows_useful_flops(inst, rows) -> float:
+    """Useful flop of the given flat rows only (the host-baseline sample)."""
+    p = inst.prefix_len
+    offs = inst.seg_offsets.astype(np.int64)
+    pairs = 0
+    for r in rows:
+        if r < p:
+            pairs += r + 1
+        else:
+            i = int(np.searchsorted(offs, r, side="right")) - 1
+            pairs += p + (r - int(offs[i])) + 1
+    return 4.0 * inst.d * inst.hq * float(pairs)
 
 
 def flat_tree_useful_flops(inst, parents) -> float:
@@ -121,15 +148,40 @@ class FlatRunner:
         self.ps.fwd_flat(self.q, self.k, self.v, self.inst.prefix_len, self.seg, self.inst.max_seg_len,
                          sm_scale=self.inst.sm_scale, out=self.o, lse=self.lse, seg_parent=self.par)
 
-    def check(self):
-        import torch
+    def outputs(self):
+        return self.o, self.lse
 
-        self()
-        torch.cuda.synchronize()
-        ok = bool(torch.isfinite(self.o).all().item() and torch.isfinite(self.lse).all().item())
-        log(f"{self.inst.name}: outputs finite: {ok}")
-        if not ok:
-            raise RuntimeError(f"{self.inst.name}: non-finite output")
+
+class PagedRunner:
+    def __init__(self, ps, inst):
+        import torch
+        from gpu_util import to_dev
+
+        self.ps, self.inst = ps, inst
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        self.q = to_dev(inst.q, inst.q_dtype)
+        self.kp = to_dev(inst.k_pool, inst.kv_dtype)
+        self.vp = to_dev(inst.v_pool, inst.kv_dtype)
+        self.kx = to_dev(inst.k_ext, inst.kv_dtype)
+        self.vx = to_dev(inst.v_ext, inst.kv_dtype)
+        self.indptr, self.indices, self.plens = i32(inst.kv_indptr), i32(inst.kv_indices), i32(inst.prefix_lens)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+        desc = ps.paged_desc(inst.batch, inst.draft_len, inst.page_size, inst.num_pages, self.plens.data_ptr(),
+                             self.indptr.data_ptr(), self.indices.data_ptr(), inst.max_prefix_len,
+                             self.kx.data_ptr(), self.vx.data_ptr())
+        nbytes = ps.psattn_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        self.info = ps.plan_info(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
+
+    def __call__(self):
+        i = self.inst
+        self.ps.fwd_paged(self.q, self.kp, self.vp, self.indptr, self.indices, self.plens, self.kx, self.vx,
+                          i.draft_len, i.max_prefix_len, sm_scale=i.sm_scale, k_scale=i.k_scale,
+                          v_scale=i.v_scale, kv_dtype=i.kv_dtype, out=self.o, lse=self.lse, workspace=self.ws)
+
+    def outputs(self):
+        return self.o, self.lse
 
 
 class MlaRunner:
@@ -151,6 +203,9 @@ class MlaRunner:
         self.ps.fwd_mla(self.q, self.ckv, self.idx, sm_scale=self.inst.sm_scale, sink=self.sink, out=self.o,
                         lse=self.lse)
 
+    def outputs(self):
+        return self.o, self.lse
+
     def useful_flops(self) -> float:
         # 4 * D per (token, head, listed key): the score and value products
         return 4.0 * self.inst.dim * self.inst.num_heads * self.n_keys
@@ -158,16 +213,6 @@ class MlaRunner:
     def gathered_bytes(self) -> float:
         # every listed latent row once per token (2 * D bytes), plus Q and O
         return float(self.n_keys * 2 * self.inst.dim + 2 * self.q.numel() * 2)
-
-    def check(self):
-        import torch
-
-        self()
-        torch.cuda.synchronize()
-        ok = bool(torch.isfinite(self.o).all().item() and torch.isfinite(self.lse).all().item())
-        log(f"{self.inst.name}: outputs finite: {ok}")
-        if not ok:
-            raise RuntimeError(f"{self.inst.name}: non-finite output")
 
 
 class BwdRunner:
@@ -199,49 +244,19 @@ class BwdRunner:
         self.ps.bwd_flat(self.q, self.k, self.v, self.o, self.lse, self.do, i.prefix_len, self.seg, i.max_seg_len,
                          sm_scale=i.sm_scale, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
 
-    def finite(self) -> bool:
-        import torch
-
-        return all(bool(torch.isfinite(t.float()).all().item()) for t in (self.dq, self.dk, self.dv))
+    def outputs(self):
+        return self.dq, self.dk, self.dv
 
 
-class PagedRunner:
-    def __init__(self, ps, inst):
-        import torch
-        from gpu_util import to_dev
+def check_finite(run, name):
+    import torch
 
-        self.ps, self.inst = ps, inst
-        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-        self.q = to_dev(inst.q, inst.q_dtype)
-        self.kp = to_dev(inst.k_pool, inst.kv_dtype)
-        self.vp = to_dev(inst.v_pool, inst.kv_dtype)
-        self.kx = to_dev(inst.k_ext, inst.kv_dtype)
-        self.vx = to_dev(inst.v_ext, inst.kv_dtype)
-        self.indptr, self.indices, self.plens = i32(inst.kv_indptr), i32(inst.kv_indices), i32(inst.prefix_lens)
-        self.o = torch.empty_like(self.q)
-        self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
-        desc = ps.paged_desc(inst.batch, inst.draft_len, 16, inst.num_pages, self.plens.data_ptr(),
-                             self.indptr.data_ptr(), self.indices.data_ptr(), inst.max_prefix_len,
-                             self.kx.data_ptr(), self.vx.data_ptr())
-        nbytes = ps.psattn_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
-        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
-        self.info = ps.plan_info(desc, inst.hq, inst.hkv, inst.d, inst.q_dtype, inst.kv_dtype)
-
-    def __call__(self):
-        i = self.inst
-        self.ps.fwd_paged(self.q, self.kp, self.vp, self.indptr, self.indices, self.plens, self.kx, self.vx,
-                          i.draft_len, i.max_prefix_len, sm_scale=i.sm_scale, k_scale=i.k_scale,
-                          v_scale=i.v_scale, kv_dtype=i.kv_dtype, out=self.o, lse=self.lse, workspace=self.ws)
-
-    def check(self):
-        import torch
-
-        self()
-        torch.cuda.synchronize()
-        ok = bool(torch.isfinite(self.o).all().item() and torch.isfinite(self.lse).all().item())
-        log(f"{self.inst.name}: outputs finite: {ok}")
-        if not ok:
-            raise RuntimeError(f"{self.inst.name}: non-finite output")
+    run()
+    torch.cuda.synchronize()
+    ok = all(bool(torch.isfinite(t.float()).all().item()) for t in run.outputs())
+    log(f"{name}: outputs finite: {ok}")
+    if not ok:
+        raise RuntimeError(f"{name}: non-finite output")
 
 
 def evict(flush):
@@ -250,8 +265,9 @@ def evict(flush):
 
 
 def time_calls(fn, flush, steps: int, warmup: int):
-    """Mean, min and p50 of per-call event times (ms), each call preceded by a
-    cache-evicting read outside the events."""
+    """Per-call event times (ms) of `steps` calls after `warmup` untimed ones,
+    each call preceded by a cache-evicting read outside its events.  The
+    events go on the current stream, the one the library launches on."""
     import torch
 
     for _ in range(warmup):
@@ -269,27 +285,51 @@ def time_calls(fn, flush, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    return dict(mean=float(ms.mean()), min=float(ms.min()), p50=float(np.median(ms)), wall_s=wall)
+    return dict(mean=float(ms.mean()), min=float(ms.min()), p10=float(np.percentile(ms, 10)),
+                p50=float(np.median(ms)), p90=float(np.percentile(ms, 90)), wall_s=wall)
 
 
-def cpu_baseline(inst, flops_fn):
-    """The float64 oracle on the host cores, on the whole GRPO workload."""
+def time_record(t, unit="us"):
+    f = 1e3 if unit == "us" else 1.0
+    return {f"{k}_{unit}": round(t[k] * f, 3) for k in ("mean", "p10", "p50", "p90", "min")}
+
+
+# ------------------------------------------------------------------ host baseline
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inst, n_rows: int):
+    """The float64 oracle (build_kv expansion + causal softmax attention) on a
+    bounded, seeded sample of the headline workload's query rows, on every
+    core this process may run on (BLAS threads set to that count)."""
     from oracle.attention import attn_flat
 
-    try:
-        from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
-        threads = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    attn_flat(inst.q, inst.k, inst.v, inst.prefix_len, inst.seg_offsets, inst.sm_scale, dtype=inst.dtype)
-    dt = time.perf_counter() - t0
-    return {"value": flops_fn(inst) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole {inst.name} workload ({inst.total_tokens} rows x {inst.hq} heads), "
-                      f"float64 build_kv expansion, {dt:.2f} s"}
+    cores = len(os.sched_getaffinity(0))
+    rows = np.sort(np.random.default_rng(12345).choice(inst.total_tokens, size=n_rows, replace=False))
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        attn_flat(inst.q, inst.k, inst.v, inst.prefix_len, inst.seg_offsets, inst.sm_scale, dtype=inst.dtype,
+                  rows=rows)
+        dt = time.perf_counter() - t0
+    flops = flat_rows_useful_flops(inst, rows)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{n_rows} seeded query rows (all {inst.hq} heads) of the {inst.name} workload "
+                      f"({inst.total_tokens} rows), float64 build_kv expansion per rollout, {dt:.2f} s "
+                      f"for {flops:.3e} useful flop"}
 
 
+# ------------------------------------------------------------------ counters
 # the sources the headline kernel (flat2_kernel) is compiled from
 HEADLINE_SOURCES = ("device_common.h", "launch.h", "plan.h", "psattn_flat.hip")
 
@@ -327,36 +367,71 @@ def traffic_from_profile(kernel_prefix: str, grid: int):
     return None
 
 
+# ------------------------------------------------------------------ sweeps
 def prefix_sweep(ps, flush, calls: int, copy_calib: bool, json_out=None):
-    """The GRPO shape with N = 1, 2, 4, 8, 16 rollouts of 512 tokens (P = 2048,
-    Hq = 32, Hkv = 8, D = 128, bf16): a few evicted calls each, for a counter
-    run that checks that the prefix K/V is read about once per call whatever
-    N is.  Prints one JSON line with, per N, the launch grid (to match the
+    """The GRPO head layouts with N = 1, 2, 4, 8, 16 rollouts of 512 tokens,
+    at P = 2048 (Hq=32, Hkv=8) and at P = 8192 (Hq=64, Hkv=8, the ragged
+    workload's), D = 128, bf16: a few evicted calls each, for a counter run
+    that checks that the prefix K/V is read about once per call whatever N
+    is.  Prints one JSON line with, per case, the launch grid (to match the
     counter rows) and the algorithmic bytes split into Q, prefix K/V and
     rollout K/V."""
     import torch
     from psattn_inputs import BF16, make_flat
 
     rows = []
-    for n in (1, 2, 4, 8, 16):
-        inst = make_flat(2048, [512] * n, 32, 8, 128, dtype=BF16, seed=200 + n, name=f"grpo_n{n}")
-        run = FlatRunner(ps, inst)
-        t = time_calls(run, flush, calls, 1)
-        tok, p = inst.total_tokens, inst.prefix_len
-        rows.append({"n": n, "grid_threads": run.grid_threads(), "calls": calls + 1, "us": round(t["mean"] * 1e3, 2),
-                     "q_bytes": tok * 32 * 128 * 2, "o_bytes": tok * 32 * 128 * 2,
-                     "prefix_kv_bytes": 2 * p * 8 * 128 * 2, "rollout_kv_bytes": 2 * (tok - p) * 8 * 128 * 2})
-        del run, inst
+    for p, hq in ((2048, 32), (8192, 64)):
+        for n in (1, 2, 4, 8, 16):
+            inst = make_flat(p, [512] * n, hq, 8, 128, dtype=BF16, seed=200 + n + p, name=f"p{p}_n{n}")
+            run = FlatRunner(ps, inst)
+            t = time_calls(run, flush, calls, 1)
+            tok = inst.total_tokens
+            rows.append({"p": p, "hq": hq, "n": n, "grid_threads": run.grid_threads(), "calls": calls + 1,
+                         "us": round(t["mean"] * 1e3, 2), "q_bytes": tok * hq * 128 * 2,
+                         "o_bytes": tok * hq * 128 * 2, "prefix_kv_bytes": 2 * p * 8 * 128 * 2,
+                         "rollout_kv_bytes": 2 * (tok - p) * 8 * 128 * 2})
+            del run, inst
     out = {"prefix_sweep": rows}
     if copy_calib:
-        n = (256 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calib_bytes"] = {"read": n * 4, "write": n * 4}
+        out["copy_calib_bytes"] = copy_calibration()
     print(json.dumps(out), file=json_out or sys.stdout, flush=True)
+
+
+def copy_calibration():
+    """A plain 256 MiB device copy (known bytes), to scale the profiler's
+    byte counters."""
+    import torch
+
+    n = (256 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"read": n * 4, "write": n * 4}
+
+
+# ------------------------------------------------------------------ main
+def flat_record(inst, t, bound_peak, bound="mfma"):
+    flops = flat_useful_flops(inst)
+    ab = flat_alg_bytes(inst)
+    tf = flops / (t["mean"] * 1e-3) / 1e12
+    gbs = ab / (t["mean"] * 1e-3) / 1e9
+    rec = {"useful_flop": flops, "alg_bytes": ab, "useful_tflops": round(tf, 2), "hbm_gbs": round(gbs, 1),
+           "bound": bound, "peak": bound_peak, "frac": round((tf if bound != "hbm" else gbs) / bound_peak, 4)}
+    rec.update(time_record(t))
+    return rec
+
+
+def paged_record(inst, t, runner):
+    flops = paged_useful_flops(inst)
+    ab = paged_alg_bytes(inst)
+    gbs = ab / (t["mean"] * 1e-3) / 1e9
+    rec = {"useful_flop": flops, "alg_bytes": ab, "useful_tflops": round(flops / (t["mean"] * 1e-3) / 1e12, 2),
+           "hbm_gbs": round(gbs, 1), "bound": "hbm", "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+           "n_splits": runner.info.n_splits, "split_len": runner.info.split_len}
+    rec.update(time_record(t))
+    return rec
 
 
 def main():
@@ -364,16 +439,18 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--all", action="store_true", help="also time the fp8 verify and ragged GRPO workloads")
+    ap.add_argument("--all", action="store_true", help="also time the two-level sharing and sparse-MLA workloads")
+    ap.add_argument("--only", default=None, help="comma-separated workload names to time (no headline line)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (known bytes) to scale profiler byte counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=6000, help="query rows of the host-baseline sample")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--prefix-sweep", action="store_true",
-                    help="instead of the benchmark: GRPO with 1..16 rollouts, for the prefix-K/V-read-once counter check")
+                    help="instead of the benchmark: GRPO shapes with 1..16 rollouts at P=2048 and P=8192, "
+                         "for the prefix-K/V-read-once counter check")
     args = ap.parse_args()
-    # the one JSON line is the only thing on stdout; progress and parity
-    # reports go to stderr
+    # the one JSON line is the only thing on stdout; progress goes to stderr
     json_out = sys.stdout
     sys.stdout = sys.stderr
     if args.gpus != 1:
@@ -392,133 +469,123 @@ def main():
         prefix_sweep(ps, flush, max(1, args.steps), args.copy_calib, json_out)
         return
 
-    log("generating grpo workload")
-    g_inst = make_config("grpo")
-    grpo = FlatRunner(ps, g_inst)
-    if not args.no_check:
-        grpo.check()
-    log("timing grpo")
-    tg = time_calls(grpo, flush, args.steps, args.warmup)
-    g_flops = flat_useful_flops(g_inst)
-    g_tflops = g_flops / (tg["mean"] * 1e-3) / 1e12
-    g_tflops_best = g_flops / (tg["min"] * 1e-3) / 1e12
-    traffic = traffic_from_profile("flat2_kernel<128, false>", grpo.grid_threads())
+    only = None if args.only is None else set(args.only.split(","))
+    want = lambda name: only is None or name in only
+    recs = {}
+    insts = {}
+
+    for name in ("tiny", "grpo", "verify16k", "verify_fp8", "grpo_ragged"):
+        if not want(name):
+            continue
+        log(f"generating {name}")
+        inst = make_config(name)
+        paged = name.startswith("verify")
+        run = PagedRunner(ps, inst) if paged else FlatRunner(ps, inst)
+        if not args.no_check:
+            check_finite(run, name)
+        steps = args.steps
+        log(f"timing {name} ({steps} calls)")
+        t = time_calls(run, flush, steps, args.warmup)
+        if paged:
+            recs[name] = paged_record(inst, t, run)
+        elif name == "tiny":
+            # fp32, 96 tokens: a single small launch, bound by latency; the
+            # fraction is against the fp32 peak for completeness
+            recs[name] = flat_record(inst, t, PEAK_F32_TFLOPS, bound="latency (fp32 peak)")
+        else:
+            recs[name] = flat_record(inst, t, PEAK_BF16_TFLOPS)
+            recs[name]["grid_threads"] = run.grid_threads()
+        if name == "grpo_ragged":
+            recs[name]["total_tokens"] = inst.total_tokens
+            insts[name] = inst
+        del run
+
+    if want("grpo_bwd"):
+        log("timing the grpo backward")
+        g_inst = make_config("grpo")
+        gb = BwdRunner(ps, g_inst)
+        if not args.no_check:
+            check_finite(gb, "grpo_bwd")
+        tb = time_calls(gb, flush, max(3, args.steps // 2), 2)
+        b_flops = 2.5 * flat_useful_flops(g_inst)  # S, dP, dV, dK, dQ: 10 D flop per visible pair and head
+        tf = b_flops / (tb["mean"] * 1e-3) / 1e12
+        recs["grpo_bwd"] = {"useful_flop": b_flops, "useful_tflops": round(tf, 2), "bound": "mfma",
+                            "peak": PEAK_BF16_TFLOPS, "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        recs["grpo_bwd"].update(time_record(tb))
+        del gb
+
+    if args.all:
+        # multi-level sharing at the GRPO shape: two shared 512-token
+        # continuations of the prompt, each continued by three rollouts
+        log("timing grpo_chain")
+        c_inst = make_flat(2048, [512] * 8, 32, 8, 128, dtype=BF16, seed=77, name="grpo_chain")
+        parents = [-1, -1, 0, 0, 0, 1, 1, 1]
+        cr = FlatRunner(ps, c_inst, seg_parent=parents)
+        if not args.no_check:
+            check_finite(cr, "grpo_chain")
+        tc = time_calls(cr, flush, args.steps, args.warmup)
+        cf = flat_tree_useful_flops(c_inst, parents)
+        recs["grpo_chain"] = {"useful_tflops": round(cf / (tc["mean"] * 1e-3) / 1e12, 2),
+                              "frac": round(cf / (tc["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "parents": parents}
+        recs["grpo_chain"].update(time_record(tc))
+        del cr
+        # sparse shared-latent MLA (DSA prefill): 16384 tokens, 64 heads,
+        # top-2048 lists over the prompt's own 512-wide latent rows
+        log("timing mla_dsa")
+        mr = MlaRunner(ps, make_config("mla_dsa"))
+        if not args.no_check:
+            check_finite(mr, "mla_dsa")
+        tm = time_calls(mr, flush, max(5, args.steps // 3), 2)
+        mf, mb = mr.useful_flops(), mr.gathered_bytes()
+        recs["mla_dsa"] = {"useful_tflops": round(mf / (tm["mean"] * 1e-3) / 1e12, 2),
+                           "frac": round(mf / (tm["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "gathered_gbs": round(mb / (tm["mean"] * 1e-3) / 1e9, 1)}
+        recs["mla_dsa"].update(time_record(tm, "ms"))
+        del mr
+
+    copy_calib = copy_calibration() if args.copy_calib else None
+
+    if only is not None or HEADLINE not in recs:
+        out = {"workloads": recs}
+        if copy_calib:
+            out["copy_calib_bytes"] = copy_calib
+        print(json.dumps(out), file=json_out, flush=True)
+        return
+
+    h = recs[HEADLINE]
+    h_inst = insts[HEADLINE]
+    ms = h["mean_us"] / 1e3
+    traffic = traffic_from_profile("flat2_kernel<128, false>", h["grid_threads"])
     out = {
         "metric": METRIC,
-        "value": round(g_tflops, 2),
+        "value": h["useful_tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(tg["mean"], 5),
+        "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "grpo: P=2048 + 8 rollouts x 512, Hq=32, Hkv=8, D=128, bf16 N(0,1), flat packed",
-                   "global_batch": 8, "seq_len": 2048 + 512, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "flat2_kernel<128, false> (bf16)",
-                     "per_launch_useful_flop": g_flops, "best_call_tflops": round(g_tflops_best, 2)},
-        "grpo_hbm_gbs": round(flat_alg_bytes(g_inst) / (tg["mean"] * 1e-3) / 1e9, 1),
+        "config": {"workload": f"grpo_ragged: P=8192 shared prompt + 16 rollouts of U{{256..1024}} tokens "
+                               f"(seed 5, T={h_inst.total_tokens}), Hq=64, Hkv=8, D=128, bf16 N(0,1) with 1% of "
+                               f"key rows x8, flat packed with seg_offsets",
+                   "global_batch": 16, "seq_len": int(h_inst.total_tokens), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": h["useful_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": h["frac"], "traffic": traffic,
+                     "kernel": "flat2_kernel<128, false> (bf16), one launch per call",
+                     "per_launch_useful_flop": h["useful_flop"]},
+        "verify_us_at_16k": recs.get("verify16k", {}).get("mean_us"),
+        "workloads": recs,
     }
-    del grpo
-
-    log("timing the grpo backward")
-    gb = BwdRunner(ps, g_inst)
-    tb = time_calls(gb, flush, max(3, args.steps // 3), 2)
-    assert gb.finite(), "non-finite gradients"
-    b_flops = 2.5 * g_flops  # S, dP, dV, dK and dQ products: 10 D flop per visible pair and query head
-    out["grpo_bwd"] = {"us": round(tb["mean"] * 1e3, 1), "us_min": round(tb["min"] * 1e3, 1),
-                       "useful_tflops": round(b_flops / (tb["mean"] * 1e-3) / 1e12, 2),
-                       "frac_mfma": round(b_flops / (tb["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                       "per_call_useful_flop": b_flops}
-    del gb
-
-    log("generating verify16k workload")
-    v_inst = make_config("verify16k")
-    ver = PagedRunner(ps, v_inst)
-    if not args.no_check:
-        ver.check()
-    log("timing verify16k")
-    tv = time_calls(ver, flush, args.steps, args.warmup)
-    vb = paged_alg_bytes(v_inst)
-    v_gbs = vb / (tv["mean"] * 1e-3) / 1e9
-    out["verify16k"] = {"us": round(tv["mean"] * 1e3, 2), "us_min": round(tv["min"] * 1e3, 2),
-                        "hbm_gbs": round(v_gbs, 1), "frac_hbm": round(v_gbs / PEAK_HBM_GBS, 4),
-                        "alg_bytes": vb, "useful_tflops": round(paged_useful_flops(v_inst) / (tv["mean"] * 1e-3) / 1e12, 2),
-                        "n_splits": ver.info.n_splits, "split_len": ver.info.split_len}
-    del ver
-
-    if args.all:
-        log("generating verify_fp8 workload")
-        f_inst = make_config("verify_fp8")
-        fr = PagedRunner(ps, f_inst)
-        if not args.no_check:
-            fr.check()
-        tf = time_calls(fr, flush, args.steps, args.warmup)
-        fb = paged_alg_bytes(f_inst)
-        out["verify_fp8"] = {"us": round(tf["mean"] * 1e3, 2), "hbm_gbs": round(fb / (tf["mean"] * 1e-3) / 1e9, 1),
-                             "frac_hbm": round(fb / (tf["mean"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                             "n_splits": fr.info.n_splits}
-        del fr
-        log("generating grpo_ragged workload")
-        r_inst = make_config("grpo_ragged")
-        rr = FlatRunner(ps, r_inst)
-        if not args.no_check:
-            rr.check()
-        tr = time_calls(rr, flush, max(5, args.steps // 3), 2)
-        rf = flat_useful_flops(r_inst)
-        out["grpo_ragged"] = {"ms": round(tr["mean"], 4), "useful_tflops": round(rf / (tr["mean"] * 1e-3) / 1e12, 2),
-                              "frac_mfma": round(rf / (tr["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del rr
-        # multi-level sharing at the GRPO shape: two shared 512-token
-        # continuations of the prompt, each continued by three rollouts
-        log("generating grpo_chain workload")
-        c_inst = make_flat(2048, [512] * 8, 32, 8, 128, dtype=BF16, seed=77, name="grpo_chain")
-        parents = [-1, -1, 0, 0, 0, 1, 1, 1]
-        cr = FlatRunner(ps, c_inst, seg_parent=parents)
-        if not args.no_check:
-            cr.check()
-        tc = time_calls(cr, flush, args.steps, args.warmup)
-        cf = flat_tree_useful_flops(c_inst, parents)
-        out["grpo_chain"] = {"us": round(tc["mean"] * 1e3, 2),
-                             "useful_tflops": round(cf / (tc["mean"] * 1e-3) / 1e12, 2),
-                             "frac_mfma": round(cf / (tc["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                             "parents": parents}
-        del cr
-
-    if args.all:
-        # sparse shared-latent MLA (DSA prefill): 16384 tokens, 64 heads,
-        # top-2048 lists over the prompt's own 512-wide latent rows
-        log("generating mla_dsa workload")
-        m_inst = make_config("mla_dsa")
-        mr = MlaRunner(ps, m_inst)
-        if not args.no_check:
-            mr.check()
-        tm = time_calls(mr, flush, max(5, args.steps // 3), 2)
-        mf = mr.useful_flops()
-        mb = mr.gathered_bytes()
-        out["mla_dsa"] = {"ms": round(tm["mean"], 4), "useful_tflops": round(mf / (tm["mean"] * 1e-3) / 1e12, 2),
-                          "frac_mfma": round(mf / (tm["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                          "gathered_gbs": round(mb / (tm["mean"] * 1e-3) / 1e9, 1)}
-        del mr
-
-    if args.copy_calib:
-        n = (256 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calib_bytes"] = {"read": n * 4, "write": n * 4}
-        del src, dst
-
+    if copy_calib:
+        out["copy_calib_bytes"] = copy_calib
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu baseline)")
-        out["cpu_baseline"] = cpu_baseline(g_inst, flat_useful_flops)
+        out["cpu_baseline"] = cpu_baseline(h_inst, args.cpu_rows)
     print(json.dumps(out), file=json_out, flush=True)
 
 
