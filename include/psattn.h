@@ -217,6 +217,26 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
                          void* stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory at
+ * call time (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): psattn_fwd with the paged split scratch taken from
+ * a fixed array of PSATTN_NOALLOC_SCRATCH_BYTES in device memory, one per GPU,
+ * instead of a caller workspace.  Arguments, layouts, results and errors are
+ * those of psattn_fwd; a descriptor whose psattn_workspace_size() exceeds
+ * PSATTN_NOALLOC_SCRATCH_BYTES returns PSATTN_E_UNSUPPORTED with nothing
+ * enqueued.  The call allocates and frees nothing; the first call on a
+ * device looks up that device's array once.  Every call on one GPU shares
+ * its array (the contents on entry do not matter, each call writes what it
+ * reads), so calls that overlap on one GPU -- on two streams, or from two
+ * threads without ordering -- race and give undefined results.
+ */
+#define PSATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+psattn_status psattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
+                                 float sm_scale, psattn_dtype q_dtype, psattn_dtype kv_dtype,
+                                 float k_scale, float v_scale, void* stream);
+
+/*
  * Backward of the flat forward (PrefixSharing PR #50, "关键变更" / key
  * changes: the rollouts' KV is built by copying the prefix with .copy_(), so
  * gradients flow back through the copies and a stored prefix row receives the

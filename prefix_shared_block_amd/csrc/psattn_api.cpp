@@ -121,6 +121,30 @@ psattn_status check_common(const psattn_desc* d, int32_t hq, int32_t hkv, int32_
   return PSATTN_OK;
 }
 
+// Everything psattn_fwd checks apart from the workspace; *empty: nothing to
+// enqueue (a valid call with no rows).
+psattn_status check_fwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                        psattn_dtype q_dtype, psattn_dtype kv_dtype, float k_scale, float v_scale, Plan* p,
+                        bool* empty) {
+  psattn_status st = check_common(desc, hq, hkv, d, q_dtype, kv_dtype, p);
+  if (st != PSATTN_OK) return st;
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(PSATTN_E_INVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
+  if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
+    return fail(PSATTN_E_INVAL, "k_scale / v_scale must be finite and > 0");
+  *empty = desc->mode == PSATTN_MODE_FLAT ? desc->total_tokens == 0 : desc->batch == 0;
+  if (*empty) return PSATTN_OK;
+  if (!q || !k || !v || !o || !lse) return fail(PSATTN_E_INVAL, "q, k, v, o and lse must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return fail(PSATTN_E_INVAL, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
+  if (desc->mode == PSATTN_MODE_PAGED && (!aligned(desc->k_ext, 4) || !aligned(desc->v_ext, 4)))
+    return fail(PSATTN_E_INVAL, "k_ext / v_ext misaligned");
+  if (desc->mode == PSATTN_MODE_FLAT && (k_scale != 1.0f || v_scale != 1.0f))
+    return fail(PSATTN_E_UNSUPPORTED, "k_scale / v_scale must be 1 in flat mode");
+  return PSATTN_OK;
+}
+
 // ---------------------------------------------------------------- backward
 constexpr int32_t kBwdRowChunk = 512;  // query tokens per dK/dV item
 
@@ -202,19 +226,10 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
                          void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   Plan p;
-  psattn_status st = check_common(desc, hq, hkv, d, q_dtype, kv_dtype, &p);
-  if (st != PSATTN_OK) return st;
-  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
-    return fail(PSATTN_E_INVAL, "sm_scale must be finite and > 0 (got %g)", (double)sm_scale);
-  if (!(k_scale > 0.f) || !std::isfinite(k_scale) || !(v_scale > 0.f) || !std::isfinite(v_scale))
-    return fail(PSATTN_E_INVAL, "k_scale / v_scale must be finite and > 0");
-  const bool empty = desc->mode == PSATTN_MODE_FLAT ? desc->total_tokens == 0 : desc->batch == 0;
-  if (empty) return PSATTN_OK;
-  if (!q || !k || !v || !o || !lse) return fail(PSATTN_E_INVAL, "q, k, v, o and lse must not be NULL");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
-    return fail(PSATTN_E_INVAL, "q/k/v/o must be 16-byte aligned and lse 4-byte aligned");
-  if (desc->mode == PSATTN_MODE_PAGED && (!aligned(desc->k_ext, 4) || !aligned(desc->v_ext, 4)))
-    return fail(PSATTN_E_INVAL, "k_ext / v_ext misaligned");
+  bool empty = false;
+  psattn_status st = check_fwd(q, k, v, o, lse, desc, hq, hkv, d, sm_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                               &p, &empty);
+  if (st != PSATTN_OK || empty) return st;
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes)
       return fail(PSATTN_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
@@ -224,8 +239,6 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
   const float log2e = 1.4426950408889634f;
   int err = 0;
   if (desc->mode == PSATTN_MODE_FLAT) {
-    if (k_scale != 1.0f || v_scale != 1.0f)
-      return fail(PSATTN_E_UNSUPPORTED, "k_scale / v_scale must be 1 in flat mode");
     FlatArgs a{};
     a.q = q;
     a.k = k;
@@ -273,6 +286,32 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
   }
   if (err) return fail(PSATTN_E_HIP, "kernel launch failed: %s", hip_error_string(err));
   return PSATTN_OK;
+}
+
+psattn_status psattn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d, float sm_scale,
+                                 psattn_dtype q_dtype, psattn_dtype kv_dtype, float k_scale, float v_scale,
+                                 void* stream) {
+  g_last_error.clear();
+  Plan p;
+  bool empty = false;
+  psattn_status st = check_fwd(q, k, v, o, lse, desc, hq, hkv, d, sm_scale, q_dtype, kv_dtype, k_scale, v_scale,
+                               &p, &empty);
+  if (st != PSATTN_OK || empty) return st;
+  if (p.ws_bytes > PSATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(PSATTN_E_UNSUPPORTED,
+                "the split scratch of %zu bytes exceeds the %zu bytes the allocation-free entry point holds "
+                "(use psattn_fwd with a workspace)",
+                p.ws_bytes, (size_t)PSATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (p.ws_bytes > 0) {
+    const int err = noalloc_scratch(&ws);
+    if (err) return fail(PSATTN_E_HIP, "scratch lookup failed: %s", hip_error_string(err));
+    ws_bytes = PSATTN_NOALLOC_SCRATCH_BYTES;
+  }
+  return psattn_fwd(q, k, v, o, lse, desc, hq, hkv, d, sm_scale, q_dtype, kv_dtype, k_scale, v_scale, ws,
+                    ws_bytes, stream);
 }
 
 size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,

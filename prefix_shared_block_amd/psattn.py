@@ -6,7 +6,7 @@ current HIP stream.  There is no fallback: if the library is missing or a call
 fails, an exception is raised.
 
 The C entry points are exposed under their own names (``psattn_fwd``,
-``psattn_workspace_size``, ``psattn_plan_dump``, ``psattn_plan_host``,
+``psattn_fwd_noalloc``, ``psattn_workspace_size``, ``psattn_plan_dump``, ``psattn_plan_host``,
 ``psattn_status_string``, ``psattn_last_error``) taking raw integers /
 pointers, plus two tensor-level helpers ``fwd_flat`` and ``fwd_paged``.
 """
@@ -85,6 +85,8 @@ def load(path: Optional[str] = None):
     ip = ctypes.POINTER(PsattnPlanInfo)
     lib.psattn_fwd.argtypes = [vp, vp, vp, vp, vp, dp, i32, i32, i32, f32, i32, i32, f32, f32, vp, sz, vp]
     lib.psattn_fwd.restype = i32
+    lib.psattn_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, dp, i32, i32, i32, f32, i32, i32, f32, f32, vp]
+    lib.psattn_fwd_noalloc.restype = i32
     lib.psattn_workspace_size.argtypes = [dp, i32, i32, i32, i32, i32]
     lib.psattn_workspace_size.restype = sz
     lib.psattn_plan_dump.argtypes = [dp, i32, i32, i32, i32, i32, vp, i64, ip, vp]
@@ -127,6 +129,13 @@ def psattn_fwd(q: int, k: int, v: int, o: int, lse: int, desc: PsattnDesc, hq: i
                workspace: int, workspace_bytes: int, stream: int) -> int:
     return int(load().psattn_fwd(q, k, v, o, lse, _ref(desc), hq, hkv, d, sm_scale, q_dtype,
                                  kv_dtype, k_scale, v_scale, workspace, workspace_bytes, stream))
+
+
+def psattn_fwd_noalloc(q: int, k: int, v: int, o: int, lse: int, desc: PsattnDesc, hq: int, hkv: int, d: int,
+                       sm_scale: float, q_dtype: int, kv_dtype: int, k_scale: float, v_scale: float,
+                       stream: int) -> int:
+    return int(load().psattn_fwd_noalloc(q, k, v, o, lse, _ref(desc), hq, hkv, d, sm_scale, q_dtype, kv_dtype,
+                                         k_scale, v_scale, stream))
 
 
 def psattn_bwd_workspace_size(desc: PsattnDesc, hq: int, hkv: int, d: int, dtype: int) -> int:
@@ -312,13 +321,15 @@ def fwd_mla(q, ckv, indices, sm_scale: Optional[float] = None, sink=None, out=No
 def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ext, draft_len: int,
               max_prefix_len: int, sm_scale: Optional[float] = None, k_scale: float = 1.0,
               v_scale: float = 1.0, kv_dtype: Optional[int] = None, out=None, lse=None, workspace=None,
-              draft_mask=None, qo_indptr=None):
+              draft_mask=None, qo_indptr=None, noalloc: bool = False):
     """Speculative-verify forward over a paged prefix.  q [B*Lx,Hq,D];
     pools [num_pages, page_size, Hkv, D]; k_ext/v_ext [B*Lx, Hkv, D]; index
     arrays int32 on the device; draft_mask: optional uint8 [B, Lx, Lx] draft
     tree on the device (None: the causal chain); qo_indptr: optional int32
     [B+1] ragged draft rows on the device, draft_len then being their upper
-    bound (q holds qo_indptr[B] rows).  Returns (o, lse)."""
+    bound (q holds qo_indptr[B] rows).  noalloc=True calls
+    psattn_fwd_noalloc (split scratch in the library's device array; no
+    workspace is allocated here).  Returns (o, lse)."""
     import torch
 
     rows, hq, d = q.shape
@@ -337,6 +348,11 @@ def fwd_paged(q, k_pool, v_pool, kv_indptr, kv_indices, prefix_lens, k_ext, v_ex
     desc = paged_desc(batch, draft_len, page_size, num_pages, _ptr(prefix_lens), _ptr(kv_indptr),
                       _ptr(kv_indices), max_prefix_len, _ptr(k_ext), _ptr(v_ext), _ptr(draft_mask),
                       _ptr(qo_indptr))
+    if noalloc:
+        check(psattn_fwd_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(out), _ptr(lse), desc, hq, hkv, d,
+                                 float(sm_scale), qdt, kvdt, float(k_scale), float(v_scale),
+                                 _stream_handle(q.device)))
+        return out, lse
     ws_bytes = psattn_workspace_size(desc, hq, hkv, d, qdt, kvdt)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)

@@ -328,3 +328,37 @@ def test_mla_binding_checks_argument_types(lib):
         ps.fwd_mla(q, ckv, torch.zeros(3, 8, dtype=torch.int32))
     with pytest.raises(ValueError):
         ps.fwd_mla(q, ckv, torch.zeros(4, 8, dtype=torch.int32), sink=torch.zeros(31))
+
+
+# ---------------------------------------------------------- allocation-free entry point
+def _call_noalloc(desc, hq=2, hkv=2, d=64, qdt=ps.F32, kvdt=ps.F32, q=FAKE, o=FAKE, lse=FAKE, ks=1.0, vs=1.0):
+    return ps.psattn_fwd_noalloc(q, FAKE, FAKE, o, lse, desc, hq, hkv, d, 0.125, qdt, kvdt, ks, vs, 0)
+
+
+def test_noalloc_rejects_scratch_beyond_its_array(lib):
+    # 64 requests x 8 kv heads x (splits) x 64 stacked rows of fp32 partials: far above the array
+    desc = _paged(batch=64, lx=8, pages=64 * 2048, mx=32768)
+    need = ps.psattn_workspace_size(desc, 64, 8, 256, ps.BF16, ps.FP8)
+    limit = 32 << 20
+    assert need > limit
+    assert _call_noalloc(desc, hq=64, hkv=8, d=256, qdt=ps.BF16, kvdt=ps.FP8) == ps.E_UNSUPPORTED
+    msg = ps.psattn_last_error()
+    assert str(need) in msg and str(limit) in msg
+
+
+@pytest.mark.parametrize("desc_kw,kw,status", [
+    (dict(lx=0), {}, ps.E_INVAL),
+    (dict(arrays=0), {}, ps.E_INVAL),
+    ({}, dict(ks=-1.0), ps.E_INVAL),
+    (dict(lx=40), dict(hq=8, hkv=2), ps.E_UNSUPPORTED),
+])
+def test_noalloc_validates_like_psattn_fwd(lib, desc_kw, kw, status):
+    args = dict(hq=8, hkv=2, d=128, qdt=ps.BF16, kvdt=ps.FP8)
+    args.update(kw)
+    assert _call_noalloc(_paged(**desc_kw), **args) == status
+
+
+def test_noalloc_empty_inputs_enqueue_nothing(lib):
+    assert _call_noalloc(ps.flat_desc(0, 0, 0, 0, 0), q=0, o=0, lse=0) == ps.OK
+    assert _call_noalloc(ps.paged_desc(0, 4, 16, 0, 0, 0, 0, 0, 0, 0), qdt=ps.BF16, kvdt=ps.BF16, q=0, o=0,
+                         lse=0) == ps.OK
