@@ -42,6 +42,9 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 // <= 2^kTauFlat and the rescale of O (wave-wide, skipped unless some row
 // moved) is rare after the first tiles.
 constexpr float kTauFlat = 8.0f;
+// Largest sum of one lane's 32 weights of a tile accepted without forming the
+// tile's row maximum (so every weight is <= 2^16 relative to the reference).
+constexpr float kSumCap = 65536.0f;
 
 template <int D>
 struct F2Cfg {
@@ -223,31 +226,46 @@ void flat2_kernel(FlatArgs a) {
           sc[kb][i] = kr < lim ? sc[kb][i] : -__builtin_inff();
         }
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[kb][i]);
-    mr = max_xor32(mr);
-    const float mx = mr * c;
-    const bool grow = mx > m_run + kTauFlat;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float mn = grow ? mx : m_run;
-      const float al = fast_exp2(m_run - mn);
-      l_run *= al;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= al;
-      m_run = mn;
-    }
+    // Weights against the current reference maximum, without forming the
+    // tile's row maximum first.  The lane's sum of its 32 weights bounds each
+    // of them; while it stays at or below kSumCap no weight can overflow and
+    // the tile is done.  Otherwise (the first tile of a row, whose reference
+    // is still kNegBig, or a score far above the reference) the row maximum
+    // is formed, the reference moved lazily as before, and the weights taken
+    // again.  (The sum is of the fp32 weights: summing their bf16 roundings
+    // instead moves the LSE by up to 2^-9 when one key dominates.)
     bf16x8_t pt[4];  // k-step ks = 2 kb + half: regs 8 half .. 8 half + 7 of sc[kb]
-    float psum = 0.f;
+    float psum;
+    auto weights = [&]() __attribute__((always_inline)) {
+      psum = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_run));
-        pt[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
-        psum += p;
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_run));
+          pt[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+          psum += p;
+        }
+    };
+    weights();
+    if (__builtin_amdgcn_ballot_w64(!(psum <= kSumCap)) != 0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mr = fmaxf(mr, sc[kb][i]);
+      mr = max_xor32(mr);
+      const float mx = mr * c;
+      const bool grow = mx > m_run + kTauFlat;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mn = grow ? mx : m_run;
+        const float al = fast_exp2(m_run - mn);
+        l_run *= al;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[db] *= al;
+        m_run = mn;
       }
+      weights();
+    }
     l_run += psum;
     // ---- O^T += V^T P^T: A operand lane (d, g) = V rows 16 ks + 8 t + 4 g + 0..3
     // of column d (t = 0, 1), by ds_read_b64_tr_b16: in-group source lane
