@@ -373,13 +373,15 @@ void paged_reg_kernel(PagedArgs a) {
 // Merge of the splits' partial results, one wave per (stacked row, 64-column
 // slice): O = v_scale * sum_s w_s O_s / sum_s w_s, LSE = ln 2 * (M + log2
 // sum_s w_s) with w_s = exp2(LSE_s - M), M = max_s LSE_s (empty splits have
-// LSE_s = -inf and weight 0).  Lane l holds one column; the partials of up to
-// MB splits are loaded together with the log-sum-exps, so that a wave costs
-// one memory round trip when n_splits <= MB.
-template <int D, int QDT>
+// LSE_s = -inf and weight 0).  Lane l takes columns 4 (l % 16) .. +3 of the
+// slice in the splits s = l / 16 (mod 4): one 16-byte load per split, up to
+// 16 splits in flight per lane; the four split groups are then summed across
+// lanes.  Lane s holds split s's log-sum-exp (n_splits <= 64).  PBF: the
+// partial O is stored in bf16 (8-byte loads).
+template <int D, int QDT, bool PBF>
 __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   constexpr int NCH = D / 64;
-  constexpr int MB = 32;
+  constexpr int MB = 16;  // splits per lane (4 groups x 16 = 64 splits at most)
   const int gw = __builtin_amdgcn_readfirstlane((int)((blockIdx.x * 256 + threadIdx.x) >> 6));
   const int lane = threadIdx.x & 63;
   if (gw >= a.batch * a.hkv * a.rows * NCH) return;
@@ -394,49 +396,53 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   const size_t qrow = (size_t)(draft_base(a.qo_indptr, b, a.draft_len) + t) * a.hq + h_kv * a.g + hl;
   const size_t prow0 = (((size_t)b * a.hkv + h_kv) * a.n_splits) * a.rows + r;
   const size_t sstride = (size_t)a.rows * D;
-  const int col = 64 * ch + lane;
-  const float* po = a.part_o + prow0 * D + col;
   const int ns = a.n_splits;
+  const int c = lane & 15;
+  const int gi = lane >> 4;
+  const size_t po = prow0 * D + 64 * ch + 4 * c;  // element offset of split 0
 
-  // lane s holds split s's log-sum-exp (n_splits <= 64)
   const float ls = lane < ns ? a.part_lse[prow0 + (size_t)lane * a.rows] : -__builtin_inff();
-  float x[MB];
-#pragma unroll
-  for (int u = 0; u < MB; ++u)
-    if (u < ns) x[u] = po[(size_t)u * sstride];
-  const float mt = wave_max(ls);
-  const float w = ls == -__builtin_inff() ? 0.f : fast_exp2(ls - mt);
-  const float wsum = wave_sum(w);
-  auto weight = [&](int sidx) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), sidx));
-  };
-
-  float acc = 0.f;
-  // an empty split (weight 0) holds zeros; its data is never multiplied
+  f32x4_t x[MB];
 #pragma unroll
   for (int u = 0; u < MB; ++u) {
-    if (u < ns) {
-      const float ws = weight(u);
-      if (ws != 0.f) acc += ws * x[u];
-    }
-  }
-  for (int s0 = MB; s0 < ns; s0 += MB) {
-#pragma unroll
-    for (int u = 0; u < MB; ++u)
-      if (s0 + u < ns) x[u] = po[(size_t)(s0 + u) * sstride];
-#pragma unroll
-    for (int u = 0; u < MB; ++u) {
-      if (s0 + u < ns) {
-        const float ws = weight(s0 + u);
-        if (ws != 0.f) acc += ws * x[u];
+    const int sp = gi + 4 * u;
+    if (sp < ns) {
+      if constexpr (PBF) {
+        const u32x2_t h = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const __bf16*>(a.part_o) + po +
+                                                           (size_t)sp * sstride);
+        x[u] = f32x4_t{__builtin_bit_cast(float, h[0] << 16), __builtin_bit_cast(float, h[0] & 0xffff0000u),
+                       __builtin_bit_cast(float, h[1] << 16), __builtin_bit_cast(float, h[1] & 0xffff0000u)};
+      } else {
+        x[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + po + (size_t)sp * sstride);
       }
     }
   }
-  const float v = acc * (wsum > 0.f ? a.v_scale / wsum : 0.f);
-  if constexpr (QDT == DT_F32)
-    reinterpret_cast<float*>(a.o)[qrow * D + col] = v;
-  else
-    reinterpret_cast<__bf16*>(a.o)[qrow * D + col] = (__bf16)v;
+  const float mt = wave_max(ls);
+  const float w = ls == -__builtin_inff() ? 0.f : fast_exp2(ls - mt);
+  const float wsum = wave_sum(w);
+  // an empty split (weight 0) holds zeros; its data is never multiplied
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < MB; ++u) {
+    const int sp = gi + 4 * u;
+    const float ws = __shfl(w, sp < 64 ? sp : 63);
+    if (sp < ns && ws != 0.f) acc += ws * x[u];
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  if (gi == 0) {
+    const float sc = wsum > 0.f ? a.v_scale / wsum : 0.f;
+    const size_t oi = qrow * D + 64 * ch + 4 * c;
+    if constexpr (QDT == DT_F32) {
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + oi) = acc * sc;
+    } else {
+      const u32x2_t v = {pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc)};
+      *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.o) + oi) = v;
+    }
+  }
   if (ch == 0 && lane == 0) a.lse[qrow] = wsum > 0.f ? (mt + fast_log2(wsum)) * kLn2 : -__builtin_inff();
 }
 
@@ -457,9 +463,11 @@ int launch_merge_t(const PagedArgs& a, int q_dtype, hipStream_t s) {
   const int64_t blocks = (waves + 3) / 4;
   if (blocks == 0) return 0;
   if (q_dtype == DT_F32)
-    hipLaunchKernelGGL((paged_merge_kernel<D, DT_F32>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((paged_merge_kernel<D, DT_F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (a.part_bf16)
+    hipLaunchKernelGGL((paged_merge_kernel<D, DT_BF16, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((paged_merge_kernel<D, DT_BF16>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((paged_merge_kernel<D, DT_BF16, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 

@@ -28,7 +28,9 @@
 //    element is read from LDS four times (LDS reads are cheap on this part);
 //  * the last split of each (request, kv head) also runs the causal draft
 //    block as one more superstage (draft row j sees draft keys 0..j);
-//  * k_scale is folded into the logit scale; v_scale is applied by the merge.
+//  * k_scale is folded into the logit scale; v_scale is applied by the merge;
+//  * the split's partial O is stored in bf16 (its LSE in fp32): half the
+//    bytes of the partials written here and read back by the merge.
 //
 // Contraction order of O^T += V^T P^T: position 8 g + 4 j + e of the 32 keys
 // of a wave (lane group g, score block j, element e) is key 16 j + 4 g + e,
@@ -355,7 +357,8 @@ void paged_wide_kernel(PagedArgs a) {
     const float inv = empty ? 0.f : 1.0f / lsum;
     const float w0 = s0 * inv, w1 = s1 * inv;
     const size_t prow = (((size_t)b * a.hkv + h_kv) * a.n_splits + it.split) * a.rows + myrow;
-    float* po = a.part_o + prow * D;
+    // the partial O in bf16: half the bytes written here and read by the merge
+    __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       const int d0 = 16 * db + 4 * g;
@@ -363,7 +366,8 @@ void paged_wide_kernel(PagedArgs a) {
       f32x4_t r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = (w0 != 0.f ? w0 * o[db][e] : 0.f) + (w1 != 0.f ? w1 * x1[e] : 0.f);
-      *reinterpret_cast<f32x4_t*>(po + d0) = r;
+      const u32x2_t v = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      *reinterpret_cast<u32x2_t*>(po + d0) = v;
     }
     if (g == 0) a.part_lse[prow] = empty ? -__builtin_inff() : mx + fast_log2(lsum);
   }

@@ -336,8 +336,8 @@ def _call_noalloc(desc, hq=2, hkv=2, d=64, qdt=ps.F32, kvdt=ps.F32, q=FAKE, o=FA
 
 
 def test_noalloc_rejects_scratch_beyond_its_array(lib):
-    # 64 requests x 8 kv heads x (splits) x 64 stacked rows of fp32 partials: far above the array
-    desc = _paged(batch=64, lx=8, pages=64 * 2048, mx=32768)
+    # 256 requests x 8 kv heads x (splits) x 64 stacked rows of partials: far above the array
+    desc = _paged(batch=256, lx=8, pages=256 * 2048, mx=32768)
     need = ps.psattn_workspace_size(desc, 64, 8, 256, ps.BF16, ps.FP8)
     limit = 32 << 20
     assert need > limit
