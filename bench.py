@@ -397,6 +397,34 @@ def prefix_sweep(ps, flush, calls: int, copy_calib: bool, json_out=None):
     print(json.dumps(out), file=json_out or sys.stdout, flush=True)
 
 
+def verify_sweep(ps, flush, calls: int, json_out=None):
+    """The fp8 verify head layout (4 requests, 8 drafts, Hq=16, Hkv=2,
+    D=256, fp8 K/V, pages of 16) at prefix lengths 4096 .. 65536: time per
+    call against K/V bytes, whose straight-line fit splits a call into a
+    fixed part (launch ramp, epilogue, tail, merge launch) and a streaming
+    part.  Prints one JSON line with, per length, the call's mean time and
+    its algorithmic bytes; a kernel trace of the same run gives the split
+    and merge launches of each length by their grids."""
+    from psattn_inputs import FP8, make_paged
+
+    rows = []
+    for plen in (4096, 8192, 16384, 32768, 65536):
+        pages = max(16384, 4 * plen // 16)
+        inst = make_paged([plen] * 4, 8, 16, 2, 256, kv_dtype=FP8, seed=400 + plen // 4096,
+                          num_pages=pages, scales=True, name=f"fp8_{plen}")
+        run = PagedRunner(ps, inst)
+        t = time_calls(run, flush, calls, 2)
+        rows.append({"prefix": plen, "n_splits": int(run.info.n_splits), "us": round(t["mean"] * 1e3, 2),
+                     "p50_us": round(t["p50"] * 1e3, 2), "alg_bytes": paged_alg_bytes(inst)})
+        del run, inst
+    xs = np.array([r["alg_bytes"] for r in rows], dtype=np.float64)
+    ys = np.array([r["us"] for r in rows], dtype=np.float64)
+    slope, icpt = np.polyfit(xs, ys, 1)
+    print(json.dumps({"verify_sweep": rows, "fit_fixed_us": round(float(icpt), 2),
+                      "fit_stream_tbs": round(float(1e-6 / slope), 3)}),
+          file=json_out or sys.stdout, flush=True)
+
+
 def copy_calibration():
     """A plain 256 MiB device copy (known bytes), to scale the profiler's
     byte counters."""
@@ -449,6 +477,9 @@ def main():
     ap.add_argument("--prefix-sweep", action="store_true",
                     help="instead of the benchmark: GRPO shapes with 1..16 rollouts at P=2048 and P=8192, "
                          "for the prefix-K/V-read-once counter check")
+    ap.add_argument("--verify-sweep", action="store_true",
+                    help="instead of the benchmark: the fp8 verify shape at prefix lengths 4096..65536, "
+                         "for a fixed-cost / streaming split of its call time")
     args = ap.parse_args()
     # the one JSON line is the only thing on stdout; progress goes to stderr
     json_out = sys.stdout
@@ -467,6 +498,9 @@ def main():
     flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     if args.prefix_sweep:
         prefix_sweep(ps, flush, max(1, args.steps), args.copy_calib, json_out)
+        return
+    if args.verify_sweep:
+        verify_sweep(ps, flush, max(1, args.steps), json_out)
         return
 
     only = None if args.only is None else set(args.only.split(","))
