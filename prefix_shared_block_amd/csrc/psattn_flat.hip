@@ -124,9 +124,17 @@ void flat2_kernel(FlatArgs a) {
   int c0 = n0 > 0 ? n_clean(r0b, r0e) : 0;
   int c1 = n1 > 0 ? n_clean(r1b, r1e) : 0;
   int nc = c0 + c1;
+  // The workgroup slots of one kv head (two per CU, spread over the CUs its
+  // XCDs hold) take its items in order, one generation of items at a time;
+  // odd generations walk the clean tiles of the first range (the prefix)
+  // last to first, so that each generation starts on the tiles the one
+  // before it read last, still in L2.  The order of the keys does not change
+  // the result (online softmax).
+  const int head_slots = (256 * C::MINB) / a.hkv > 0 ? (256 * C::MINB) / a.hkv : 1;
+  const bool rev = ((j / head_slots) & 1) != 0;
   auto tile_range = [&](int n, int& k0, int& ke) __attribute__((always_inline)) {
     if (n < c0) {
-      k0 = r0b + n * BN;
+      k0 = r0b + (rev ? c0 - 1 - n : n) * BN;
       ke = r0e;
     } else if (n < nc) {
       k0 = r1b + (n - c0) * BN;
