@@ -183,7 +183,9 @@ enum {
 
 /*
  * Bytes of scratch the forward call needs for this descriptor (0 in flat
- * mode; paged mode: per-split partial O and LSE in fp32, the first stage's
+ * mode; paged mode: per-split partial O (bf16 for the streaming split
+ * passes that serve bf16 and fp8 caches in pages of >= 16 slots with up to
+ * 64 stacked rows, fp32 otherwise) and its LSE in fp32, the first stage's
  * output that the second stage merges, sglang PR #27382 report, "实现拆解").
  * The caller owns this memory and passes it to every call, so the library
  * keeps no buffer of its own between calls (that report's review section,

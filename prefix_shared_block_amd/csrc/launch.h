@@ -37,7 +37,7 @@ struct PagedArgs {
   const int32_t* kv_indices;
   float* part_o;    // [B, Hkv, n_splits, R, D]  normalised partial outputs (fp32, or bf16 with part_bf16)
   float* part_lse;  // [B, Hkv, n_splits, R]     log2-domain partial LSE
-  int32_t part_bf16;  // 1: part_o holds bf16 (the 17..64-row split pass and its merge)
+  int32_t part_bf16;  // 1: part_o holds bf16 (the register and wide split passes and their merge)
   int32_t batch;
   int32_t draft_len;
   int32_t page_size;

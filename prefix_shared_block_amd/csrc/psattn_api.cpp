@@ -114,9 +114,10 @@ psattn_status check_common(const psattn_desc* d, int32_t hq, int32_t hkv, int32_
     plan->paged_blocks = (int64_t)d->batch * hkv * plan->sp.n_splits;
     if (plan->paged_blocks > INT32_MAX) return fail(PSATTN_E_UNSUPPORTED, "grid too large");
     const size_t prow = (size_t)d->batch * hkv * plan->sp.n_splits * plan->pg.rows;
-    // the 17..64-row split pass keeps its partial O in bf16 (half the bytes
-    // written and read back by the merge), the others in fp32
-    const size_t pes = plan->pg.stream == 3 ? 2 : 4;
+    // the register and wide split passes (stream 2, 3) keep their partial O
+    // in bf16 (half the bytes written and read back by the merge), the
+    // others in fp32
+    const size_t pes = (plan->pg.stream == 2 || plan->pg.stream == 3) ? 2 : 4;
     const size_t o_bytes = round_up(prow * hd * pes, kWsAlign);
     plan->ws_lse_offset = o_bytes;
     plan->ws_bytes = d->batch == 0 ? 0 : o_bytes + round_up(prow * sizeof(float), kWsAlign);
@@ -272,7 +273,7 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
     a.kv_indices = desc->kv_indices;
     a.part_o = reinterpret_cast<float*>(workspace);
     a.part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + p.ws_lse_offset);
-    a.part_bf16 = p.pg.stream == 3 ? 1 : 0;
+    a.part_bf16 = (p.pg.stream == 2 || p.pg.stream == 3) ? 1 : 0;
     a.batch = desc->batch;
     a.draft_len = desc->draft_len;
     a.page_size = desc->page_size;

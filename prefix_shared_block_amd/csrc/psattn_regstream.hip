@@ -39,7 +39,9 @@
 //    combine stage;
 //  * online softmax in the log2 domain with lazy rescaling (the running
 //    maximum only moves when a row's new maximum exceeds it by more than
-//    kTau, so every exp2 argument stays <= kTau).
+//    kTau, so every exp2 argument stays <= kTau);
+//  * the split's normalised partial O is stored in bf16 (its LSE in fp32):
+//    half the bytes written here and read back by the merge.
 //
 // LDS tiles are row-major [16 keys][D bf16] with 16-byte chunks XOR-swizzled
 // per row (K: chunk ^ (row % CPR); V: chunk ^ (2 row % CPR)).
@@ -321,9 +323,12 @@ void paged_reg_kernel(PagedArgs a) {
       const bool empty = !(lt > 0.f);
       const float inv = empty ? 0.f : 1.0f / lt;
       const size_t prow = (((size_t)b * a.hkv + h_kv) * a.n_splits + it.split) * a.rows + q16;
-      float* po = a.part_o + prow * D;
+      __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) *reinterpret_cast<f32x4_t*>(po + 16 * db + 4 * g) = o[db] * inv;
+      for (int db = 0; db < C::NDB; ++db) {
+        const f32x4_t r = o[db] * inv;
+        *reinterpret_cast<u32x2_t*>(po + 16 * db + 4 * g) = u32x2_t{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+      }
       if (g == 0) a.part_lse[prow] = empty ? -__builtin_inff() : m_run + fast_log2(lt);
     }
   } else {
@@ -364,7 +369,9 @@ void paged_reg_kernel(PagedArgs a) {
       const bool empty = !(lsum > 0.f);
       const float inv = empty ? 0.f : 1.0f / lsum;
       const size_t prow = (((size_t)b * a.hkv + h_kv) * a.n_splits + it.split) * a.rows + r;
-      *reinterpret_cast<f32x4_t*>(a.part_o + prow * D + 4 * c4) = acc * inv;
+      const f32x4_t ov = acc * inv;
+      *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.part_o) + prow * D + 4 * c4) =
+          u32x2_t{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
       if (c4 == 0) a.part_lse[prow] = empty ? -__builtin_inff() : mx + fast_log2(lsum);
     }
   }
@@ -376,9 +383,10 @@ void paged_reg_kernel(PagedArgs a) {
 // LSE_s = -inf and weight 0).  Lane l takes columns 4 (l % 16) .. +3 of the
 // slice in the splits s = l / 16 (mod 4): one 16-byte load per split, up to
 // 16 splits in flight per lane; the four split groups are then summed across
-// lanes.  Lane s holds split s's log-sum-exp (n_splits <= 64).  PBF: the
-// partial O is stored in bf16 (8-byte loads).
-template <int D, int QDT, bool PBF>
+// lanes.  Lane s holds split s's log-sum-exp (n_splits <= 64).  The split
+// passes that feed it (register and wide streaming) store their partial O in
+// bf16 (8-byte loads here); the queries, and so O, are bf16.
+template <int D>
 __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   constexpr int NCH = D / 64;
   constexpr int MB = 16;  // splits per lane (4 groups x 16 = 64 splits at most)
@@ -407,14 +415,10 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   for (int u = 0; u < MB; ++u) {
     const int sp = gi + 4 * u;
     if (sp < ns) {
-      if constexpr (PBF) {
-        const u32x2_t h = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const __bf16*>(a.part_o) + po +
-                                                           (size_t)sp * sstride);
-        x[u] = f32x4_t{__builtin_bit_cast(float, h[0] << 16), __builtin_bit_cast(float, h[0] & 0xffff0000u),
-                       __builtin_bit_cast(float, h[1] << 16), __builtin_bit_cast(float, h[1] & 0xffff0000u)};
-      } else {
-        x[u] = *reinterpret_cast<const f32x4_t*>(a.part_o + po + (size_t)sp * sstride);
-      }
+      const u32x2_t h = *reinterpret_cast<const u32x2_t*>(reinterpret_cast<const __bf16*>(a.part_o) + po +
+                                                         (size_t)sp * sstride);
+      x[u] = f32x4_t{__builtin_bit_cast(float, h[0] << 16), __builtin_bit_cast(float, h[0] & 0xffff0000u),
+                     __builtin_bit_cast(float, h[1] << 16), __builtin_bit_cast(float, h[1] & 0xffff0000u)};
     }
   }
   const float mt = wave_max(ls);
@@ -436,12 +440,8 @@ __global__ __launch_bounds__(256) void paged_merge_kernel(PagedArgs a) {
   if (gi == 0) {
     const float sc = wsum > 0.f ? a.v_scale / wsum : 0.f;
     const size_t oi = qrow * D + 64 * ch + 4 * c;
-    if constexpr (QDT == DT_F32) {
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(a.o) + oi) = acc * sc;
-    } else {
-      const u32x2_t v = {pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc)};
-      *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.o) + oi) = v;
-    }
+    const u32x2_t v = {pack_bf16x2(acc[0] * sc, acc[1] * sc), pack_bf16x2(acc[2] * sc, acc[3] * sc)};
+    *reinterpret_cast<u32x2_t*>(reinterpret_cast<__bf16*>(a.o) + oi) = v;
   }
   if (ch == 0 && lane == 0) a.lse[qrow] = wsum > 0.f ? (mt + fast_log2(wsum)) * kLn2 : -__builtin_inff();
 }
@@ -458,16 +458,11 @@ int launch_t(const PagedArgs& a, int64_t n_blocks, hipStream_t s) {
 }
 
 template <int D>
-int launch_merge_t(const PagedArgs& a, int q_dtype, hipStream_t s) {
+int launch_merge_t(const PagedArgs& a, hipStream_t s) {
   const int64_t waves = (int64_t)a.batch * a.hkv * a.rows * (D / 64);
   const int64_t blocks = (waves + 3) / 4;
   if (blocks == 0) return 0;
-  if (q_dtype == DT_F32)
-    hipLaunchKernelGGL((paged_merge_kernel<D, DT_F32, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else if (a.part_bf16)
-    hipLaunchKernelGGL((paged_merge_kernel<D, DT_BF16, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((paged_merge_kernel<D, DT_BF16, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((paged_merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, a);
   return (int)hipGetLastError();
 }
 
@@ -475,11 +470,11 @@ int launch_merge_t(const PagedArgs& a, int q_dtype, hipStream_t s) {
 
 int launch_paged_merge(const PagedArgs& a, int d, int q_dtype, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (a.n_splits > 64) return (int)hipErrorInvalidValue;
+  if (a.n_splits > 64 || q_dtype != DT_BF16 || !a.part_bf16) return (int)hipErrorInvalidValue;
   switch (d) {
-    case 64: return launch_merge_t<64>(a, q_dtype, s);
-    case 128: return launch_merge_t<128>(a, q_dtype, s);
-    case 256: return launch_merge_t<256>(a, q_dtype, s);
+    case 64: return launch_merge_t<64>(a, s);
+    case 128: return launch_merge_t<128>(a, s);
+    case 256: return launch_merge_t<256>(a, s);
   }
   return (int)hipErrorInvalidValue;
 }
