@@ -60,6 +60,16 @@ def test_grpo_rollout_count_sampled(gpu_lib, n):
     _flat_check(gpu_lib, inst, rows=_sample_rows(inst))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_flat_reversed_prefix_walk_every_row(gpu_lib, d):
+    # 64 kv heads leave 512 / 64 = 8 workgroup slots per head, so items 8..15
+    # of every head (a second generation) walk the prefix's clean tiles last
+    # to first; G = 1 gives 128-token tiles: 8 prefix items and 9 rollout
+    # items per head.  Every row is compared.
+    inst = make_flat(1000, [300, 300, 257], 64, 64, d, dtype=BF16, seed=31 + d, name=f"rev_walk_d{d}")
+    _flat_check(gpu_lib, inst)
+
+
 def test_grpo_ragged_fullsize_sampled(gpu_lib):
     inst = make_config("grpo_ragged")
     _flat_check(gpu_lib, inst, rows=_sample_rows(inst, n_random=24))
