@@ -161,6 +161,22 @@ def test_verify_gqa_ratios(gpu_lib, hq, hkv):
     _paged_check(gpu_lib, inst, label=f"verify GQA {hq}/{hkv}")
 
 
+@pytest.mark.parametrize("prefix_len,lx,hq,hkv,d,kvdt", [
+    (8192, 4, 4, 1, 128, BF16),    # 16 stacked rows: register streaming
+    (32768, 2, 16, 1, 128, FP8),   # 32 stacked rows: wide streaming
+])
+def test_verify_sixty_four_splits(gpu_lib, prefix_len, lx, hq, hkv, d, kvdt):
+    # one request and one kv head: the planner takes its largest split count,
+    # 64, the most the merge holds (one split weight per lane)
+    inst = make_paged([prefix_len], lx, hq, hkv, d, kv_dtype=kvdt, seed=95, num_pages=prefix_len // 16 + 8,
+                      scales=kvdt == FP8, name=f"splits64_{kind_of(BF16, kvdt)}")
+    fake = 256
+    info = gpu_lib.plan_info(gpu_lib.paged_desc(1, lx, inst.page_size, inst.num_pages, fake, fake, fake, prefix_len,
+                                                fake, fake), hq, hkv, d, inst.q_dtype, inst.kv_dtype)
+    assert info.n_splits == 64
+    _paged_check(gpu_lib, inst)
+
+
 @pytest.mark.parametrize("prefix_lens,lx,hq,hkv,d,kvdt", [
     ([1000, 0, 17, 4096, 33], 3, 8, 2, 128, BF16),   # ragged, empty, partial pages
     ([300, 301], 1, 4, 4, 64, BF16),                  # Lx = 1, Hq = Hkv
