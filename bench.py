@@ -337,16 +337,22 @@ HEADLINE_SOURCES = ("device_common.h", "launch.h", "plan.h", "psattn_flat.hip")
 
 
 def _headline_text(name: str, text: bytes) -> bytes:
-    if name != "launch.h":
-        return text
-    i = text.index(b"struct FlatArgs {")
-    return text[i:text.index(b"};", i) + 2]
+    """The code of one source: comments dropped and whitespace collapsed,
+    launch.h reduced to FlatArgs."""
+    import re
+
+    if name == "launch.h":
+        i = text.index(b"struct FlatArgs {")
+        text = text[i:text.index(b"};", i) + 2]
+    text = re.sub(rb"/\*.*?\*/", b" ", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b" ", text)
+    return b" ".join(text.split())
 
 
 def kernel_source_digest() -> str:
-    """sha256 over the headline kernel's sources (sorted by name; launch.h
-    reduced to FlatArgs): profiler counters are only reused while this
-    digest is unchanged."""
+    """sha256 over the code of the headline kernel's sources (sorted by name;
+    comments and whitespace ignored, launch.h reduced to FlatArgs): profiler
+    counters are only reused while this digest is unchanged."""
     import hashlib
 
     csrc = os.path.join(ROOT, "prefix_shared_block_amd", "csrc")

@@ -9,11 +9,14 @@
 //
 //  * 4 waves x 32 stacked query rows; Q^T fragments stay in registers;
 //  * the item's key ranges (the prefix, then the rollout's own keys) are
-//    walked in 64-key tiles.  Each tile's K and V rows are copied global ->
-//    LDS by global_load_lds_dwordx4 (no register staging, no VALU), one tile
-//    ahead of the arithmetic in a double buffer; the 16-byte chunks of a row
-//    land XOR-swizzled (the global address is permuted, the LDS side is
-//    contiguous), so the operand reads below avoid bank conflicts;
+//    walked in 64-key tiles (the prefix's fully visible tiles last to first
+//    in every other generation of a head's items, so that a generation
+//    starts on the tiles its predecessor left in L2).  Each tile's K and V
+//    rows are copied global -> LDS by global_load_lds_dwordx4 (no register
+//    staging, no VALU), one tile ahead of the arithmetic in a double buffer;
+//    the 16-byte chunks of a row land XOR-swizzled (the global address is
+//    permuted, the LDS side is contiguous), so the operand reads below avoid
+//    bank conflicts;
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 K rows from LDS), so a
 //    lane holds 16 scores of its own query row; online softmax in the log2
 //    domain.  The reference maximum is moved lazily (see kTauFlat), and the
