@@ -226,8 +226,9 @@ psattn_status psattn_fwd(const void* q, const void* k, const void* v, void* o, f
  * instead of a caller workspace.  Arguments, layouts, results and errors are
  * those of psattn_fwd; a descriptor whose psattn_workspace_size() exceeds
  * PSATTN_NOALLOC_SCRATCH_BYTES returns PSATTN_E_UNSUPPORTED with nothing
- * enqueued.  The call allocates and frees nothing; the first call on a
- * device looks up that device's array once.  Every call on one GPU shares
+ * enqueued.  The call allocates and frees nothing; the array used is that of
+ * the stream's device, whose address the first call on that device looks up
+ * once (making the device current for the lookup only).  Every call on one GPU shares
  * its array (the contents on entry do not matter, each call writes what it
  * reads), so calls that overlap on one GPU -- on two streams, or from two
  * threads without ordering -- race and give undefined results.

@@ -108,8 +108,9 @@ int launch_paged_combine(const PagedArgs& a, int d, int q_dtype, int kv_dtype, v
 int launch_plan_dump(int mode, const FlatArgs* fa, const PagedArgs* pa, int64_t n_items,
                      int32_t* items, void* stream);
 const char* hip_error_string(int err);
-// device address of the current device's allocation-free scratch array
-// (PSATTN_NOALLOC_SCRATCH_BYTES), defined in psattn_noalloc.hip
-int noalloc_scratch(void** ptr);
+// device address of the allocation-free scratch array
+// (PSATTN_NOALLOC_SCRATCH_BYTES) on the device of `stream`, defined in
+// psattn_noalloc.hip
+int noalloc_scratch(void* stream, void** ptr);
 
 }  // namespace psattn

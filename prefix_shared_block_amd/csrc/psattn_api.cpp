@@ -311,7 +311,7 @@ psattn_status psattn_fwd_noalloc(const void* q, const void* k, const void* v, vo
   void* ws = nullptr;
   size_t ws_bytes = 0;
   if (p.ws_bytes > 0) {
-    const int err = noalloc_scratch(&ws);
+    const int err = noalloc_scratch(stream, &ws);
     if (err) return fail(PSATTN_E_HIP, "scratch lookup failed: %s", hip_error_string(err));
     ws_bytes = PSATTN_NOALLOC_SCRATCH_BYTES;
   }
