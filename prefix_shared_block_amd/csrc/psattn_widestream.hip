@@ -16,7 +16,10 @@
 //  * each wave converts its block to bf16 once (fp8 codes exactly) into a
 //    shared, double-buffered LDS superstage tile, one superstage ahead of
 //    the arithmetic (so LDS writes overlap the MFMA work); one barrier per
-//    superstage;
+//    superstage.  With fp8 K at D = 128 or 256 the K rows stay fp8 in LDS
+//    (half the bytes written and read, no conversion) and the scores run on
+//    v_mfma_f32_16x16x128_f8f6f4 against the query rows split into two fp8
+//    terms (below);
 //  * wave (rq, kh) computes stacked rows 16 rq .. 16 rq + 15 against keys
 //    32 kh .. 32 kh + 31 of the superstage with v_mfma_f32_16x16x32_bf16:
 //    S^T = K Q^T (K rows from LDS, Q^T fragments in registers), online
@@ -70,7 +73,37 @@ struct WCfg {
   static_assert(CPR <= 64 && NB >= 1, "shape");
   __device__ static constexpr int fk(int r) { return r & (TCPR - 1); }
   __device__ static constexpr int fv(int r) { return (2 * r) & (TCPR - 1); }
+  // fp8 K with D a multiple of 128: K stays fp8 in LDS (rows of D bytes) and
+  // the scores run on v_mfma_f32_16x16x128_f8f6f4 against the query split
+  // into two fp8 terms
+  static constexpr bool F8S = KDT == DT_FP8 && D % 128 == 0;
+  static constexpr int KROWB = F8S ? D : TROWB;  // LDS bytes of a K row
+  static constexpr int KCPR = KROWB / 16;
+  static constexpr int NSD = D / 128;            // 128-deep k-steps of the fp8 score product
+  __device__ static constexpr int fk8(int r) { return r & (KCPR - 1); }
 };
+
+typedef int i8v_t __attribute__((ext_vector_type(8)));
+
+// gfx950 fp8 forms, kept in device functions (the host pass of a kernel body
+// that names them directly drops the kernel)
+// fp8 (e4m3) codes of x0..x3 in bytes 0..3, and their decoded values
+__device__ __forceinline__ int fp8x4_split(float x0, float x1, float x2, float x3, float& h0, float& h1, float& h2,
+                                           float& h3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  h0 = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+  h1 = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+  h2 = __builtin_amdgcn_cvt_f32_fp8(w, 2);
+  h3 = __builtin_amdgcn_cvt_f32_fp8(w, 3);
+  return w;
+}
+// 16 x 16 x 128 fp8 x fp8 product, unscaled
+__device__ __forceinline__ f32x4_t mfma_fp8_16x16x128(const i8v_t a, const i8v_t b, const f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// the exponent e of x = f 2^e, f in [1/2, 1)
+__device__ __forceinline__ int frexp_exponent(float x) { return __builtin_amdgcn_frexp_expf(x); }
 
 // 16 bytes of a global row (chunk pos) -> the row's LDS tile slot(s), as bf16
 template <int KDT>
@@ -144,15 +177,58 @@ void paged_wide_kernel(PagedArgs a) {
 
   // ---- query fragments (B operand of S^T = K Q^T): row 16 rq + q16,
   // k-step s, lane group g holds head-dim elements 32 s + 8 g .. +8
-  bf16x8_t qf[C::NSTEP];
+  bf16x8_t qf[C::F8S ? 1 : C::NSTEP];
+  // F8S: Q^T as the B operand of the fp8 product, k-step sd, lane group g
+  // holding head-dim elements 128 sd + 32 g .. +32, each row scaled by a power
+  // of two 2^qe that puts its largest magnitude in [128, 256) and split into
+  // hi = fp8(x) and lo = fp8(x - hi), which sum to x exactly wherever
+  // |x| >= 1/4 (a bf16 value has 8 significant bits, each fp8 term 4) and to
+  // within 2^-10 below; cq = the logit scale over 2^qe.
+  i8v_t qh[C::F8S ? C::NSD : 1], ql[C::F8S ? C::NSD : 1];
+  float cq = a.scale_log2;
   auto load_q = [&]() {
     const int rc = myrow < a.rows && myrow / a.g < qn ? myrow : 0;
     const int t = rc / a.g;
     const int hl = rc - t * a.g;
     const size_t qrow = (size_t)(qb + t) * a.hq + h_kv * a.g + hl;
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
+    if constexpr (C::F8S) {
+      float x[C::NSD][32];
+      float am = 0.f;
 #pragma unroll
-    for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
+      for (int sd = 0; sd < C::NSD; ++sd)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 128 * sd + 32 * g + 8 * u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            // bf16 element e: the high or low half of dword e / 2, as fp32 bits
+            const uint32_t w = v[e >> 1];
+            x[sd][8 * u + e] = __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+            am = fmaxf(am, fabsf(x[sd][8 * u + e]));
+          }
+        }
+      am = fmaxf(am, __shfl_xor(am, 16));
+      am = fmaxf(am, __shfl_xor(am, 32));
+      // am = f 2^ex with f in [1/2, 1): scale by 2^(8 - ex)
+      const int qe = am > 0.f ? 8 - frexp_exponent(am) : 0;
+      cq = a.scale_log2 * __builtin_ldexpf(1.0f, -qe);
+#pragma unroll
+      for (int sd = 0; sd < C::NSD; ++sd)
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const float x0 = __builtin_ldexpf(x[sd][4 * w], qe);
+          const float x1 = __builtin_ldexpf(x[sd][4 * w + 1], qe);
+          const float x2 = __builtin_ldexpf(x[sd][4 * w + 2], qe);
+          const float x3 = __builtin_ldexpf(x[sd][4 * w + 3], qe);
+          float h0, h1, h2, h3, l0, l1, l2, l3;
+          qh[sd][w] = fp8x4_split(x0, x1, x2, x3, h0, h1, h2, h3);
+          ql[sd][w] = fp8x4_split(x0 - h0, x1 - h1, x2 - h2, x3 - h3, l0, l1, l2, l3);
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
+    }
   };
 
   // superstage m: this wave's aligned 8-key block (keys k0 + 8 wave ..);
@@ -209,7 +285,10 @@ void paged_wide_kernel(PagedArgs a) {
       const int r = C::RPI * j + rr;
       if (C::RPI * NLK <= 8 || r < 8) {
         const int row = 8 * wave + r;
-        wput<KDT>(kt + row * C::TROWB, pos, C::fk(row), kd[j]);
+        if constexpr (C::F8S)
+          *reinterpret_cast<u32x4_t*>(kt + row * C::KROWB + 16 * (pos ^ C::fk8(row))) = kd[j];
+        else
+          wput<KDT>(kt + row * C::TROWB, pos, C::fk(row), kd[j]);
         wput<KDT>(vt + row * C::TROWB, pos, C::fv(row), vd[j]);
       }
     }
@@ -220,9 +299,8 @@ void paged_wide_kernel(PagedArgs a) {
   f32x4_t o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const float c = a.scale_log2;
-
   auto math = [&](int n, const char* kt, const char* vt) {
+    const float c = cq;  // logit scale (log2 domain) of this lane's row
     // keys 32 kh .. 32 kh + 31 of superstage n; lim = keys of the half that
     // this lane's row may see
     const int kofs = 32 * kh;
@@ -235,11 +313,24 @@ void paged_wide_kernel(PagedArgs a) {
     for (int j = 0; j < 2; ++j) {
       sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const int kr = kofs + 16 * j + q16;
-      const char* krow = kt + kr * C::TROWB;
+      if constexpr (C::F8S) {
+        // A operand: key row kr, head-dim bytes 128 sd + 32 g .. +32 (two chunks)
+        const char* krow = kt + kr * C::KROWB;
 #pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) {
-        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((4 * s + g) ^ C::fk(kr)));
-        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[j], 0, 0, 0);
+        for (int sd = 0; sd < C::NSD; ++sd) {
+          const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(krow + 16 * ((8 * sd + 2 * g) ^ C::fk8(kr)));
+          const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(krow + 16 * ((8 * sd + 2 * g + 1) ^ C::fk8(kr)));
+          const i8v_t kf = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3], (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+          sc[j] = mfma_fp8_16x16x128(kf, qh[sd], sc[j]);
+          sc[j] = mfma_fp8_16x16x128(kf, ql[sd], sc[j]);
+        }
+      } else {
+        const char* krow = kt + kr * C::TROWB;
+#pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(krow + 16 * ((4 * s + g) ^ C::fk(kr)));
+          sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc[j], 0, 0, 0);
+        }
       }
     }
     float mr = -__builtin_inff();
@@ -309,7 +400,8 @@ void paged_wide_kernel(PagedArgs a) {
   // retire the query loads (the oldest) before the loop, so that the
   // compiler's wait counts inside it stay exact
 #pragma unroll
-  for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(qf[s]));
+  for (int s = 0; s < (C::F8S ? 0 : C::NSTEP); ++s) asm volatile("" ::"v"(qf[s]));
+  // (the fp8 split consumes every query load inside load_q)
   if (nst > 0) put(kr[0], vr[0], tiles[0][0], tiles[0][1]);
   issue(NB, kr[0], vr[0]);
   __syncthreads();

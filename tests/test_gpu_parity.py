@@ -88,6 +88,7 @@ def test_grpo_ragged_small_full_with_outliers(gpu_lib):
     (130, [3, 200], 12, 4, 128, BF16),            # G = 3 (42-token tiles)
     (96, [40, 41], 32, 2, 256, BF16),             # D = 256, G = 16
     (77, [19, 64], 64, 1, 64, BF16),              # G = 64 (2-token tiles)
+    (40, [9, 10], 128, 1, 64, BF16),              # G = 128, the largest group (1-token tiles)
     (1, [], 2, 1, 64, BF16),                      # prefix of one token only
     (0, [1], 1, 1, 128, BF16),                    # a single token in total
     (70, [15, 33], 4, 2, 128, F32),               # fp32, D = 128
