@@ -11,7 +11,7 @@ import math
 import numpy as np
 import pytest
 
-from gpu_util import compare, kind_of, run_flat, run_paged, sample_rows as _sample_rows, to_f64
+from gpu_util import compare, kind_of, run_flat, run_paged, sample_rows as _sample_rows, to_dev, to_f64
 from oracle.attention import attn_flat, attn_paged
 from psattn_inputs import (BF16, F32, FP8, make_config, make_flat, make_flat_random_lens, make_flat_spikes,
                            make_paged, make_paged_spikes)
@@ -255,6 +255,54 @@ def test_verify_workspace_reused_across_calls(gpu_lib):
                             kv_dtype=inst.kv_dtype, page_size=inst.page_size)
         compare(to_f64(o), to_f64(lse), ro, rl, kind_of(inst.q_dtype, inst.kv_dtype),
                 f"reused workspace {list(inst.prefix_lens)[:4]} Lx={inst.draft_len} D={inst.d}")
+
+
+def test_verify_register_pass_graph_replays(gpu_lib):
+    """A captured verify call (register split pass and merge) replays to the
+    eager result: three replays, each after an eager call with other inputs
+    on the same workspace and then once more straight after, equal the eager
+    call on the same inputs bit for bit."""
+    import torch
+
+    inst = make_paged([1500, 2300, 40, 800] * 2, 4, 16, 4, 128, kv_dtype=BF16, seed=68, num_pages=600)
+    other = make_paged([1500, 2300, 40, 800] * 2, 4, 16, 4, 128, kv_dtype=BF16, seed=69, num_pages=600)
+    assert inst.draft_len * inst.hq // inst.hkv == 16  # 16 stacked rows: the register split pass
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+    def args_of(x):
+        return (to_dev(x.q, x.q_dtype), to_dev(x.k_pool, x.kv_dtype), to_dev(x.v_pool, x.kv_dtype),
+                i32(x.kv_indptr), i32(x.kv_indices), i32(x.prefix_lens), to_dev(x.k_ext, x.kv_dtype),
+                to_dev(x.v_ext, x.kv_dtype), x.draft_len, x.max_prefix_len)
+
+    a1, a2 = args_of(inst), args_of(other)
+    kw = dict(sm_scale=inst.sm_scale, kv_dtype=BF16)
+    desc = gpu_lib.paged_desc(inst.batch, 4, 16, inst.num_pages, 1, 1, 1, inst.max_prefix_len, 1, 1)
+    ws = torch.full((gpu_lib.psattn_workspace_size(desc, 16, 4, 128, BF16, BF16),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    o_e, l_e = gpu_lib.fwd_paged(*a1, **kw, workspace=ws)
+    torch.cuda.synchronize()
+    compare(to_f64(o_e), to_f64(l_e), *attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr,
+                                                  inst.kv_indices, inst.prefix_lens, inst.k_ext, inst.v_ext,
+                                                  inst.draft_len, inst.sm_scale, q_dtype=BF16, kv_dtype=BF16),
+            "bf16", "register pass, eager")
+    o_g, l_g = torch.empty_like(o_e), torch.empty_like(l_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        gpu_lib.fwd_paged(*a1, **kw, out=o_g, lse=l_g, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        gpu_lib.fwd_paged(*a2, **kw, workspace=ws)  # other partials left in the workspace
+        o_g.fill_(float("nan"))
+        l_g.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] replay {rep}", flush=True)
+        assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), f"replay {rep} differs from the eager call"
+        graph.replay()  # straight after a replay
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(l_g, l_e), f"second replay {rep} differs"
 
 
 def test_verify_zero_queries_closed_form(gpu_lib):
