@@ -186,6 +186,10 @@ void paged_wide_kernel(PagedArgs a) {
   // within 2^-10 below; cq = the logit scale over 2^qe.
   i8v_t qh[C::F8S ? C::NSD : 1], ql[C::F8S ? C::NSD : 1];
   float cq = a.scale_log2;
+  // F8S: the query row's 16-byte pieces, fetched before the first
+  // superstage's loads are issued and split after them, so that the split
+  // waits only for the query and the K/V latency runs under it
+  u32x4_t qraw[C::F8S ? C::NSD : 1][4];
   auto load_q = [&]() {
     const int rc = myrow < a.rows && myrow / a.g < qn ? myrow : 0;
     const int t = rc / a.g;
@@ -193,21 +197,30 @@ void paged_wide_kernel(PagedArgs a) {
     const size_t qrow = (size_t)(qb + t) * a.hq + h_kv * a.g + hl;
     const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + qrow * D;
     if constexpr (C::F8S) {
+#pragma unroll
+      for (int sd = 0; sd < C::NSD; ++sd)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) qraw[sd][u] = *reinterpret_cast<const u32x4_t*>(qp + 128 * sd + 32 * g + 8 * u);
+    } else {
+#pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
+    }
+  };
+  auto split_q = [&]() {
+    if constexpr (C::F8S) {
       float x[C::NSD][32];
       float am = 0.f;
 #pragma unroll
       for (int sd = 0; sd < C::NSD; ++sd)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qp + 128 * sd + 32 * g + 8 * u);
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             // bf16 element e: the high or low half of dword e / 2, as fp32 bits
-            const uint32_t w = v[e >> 1];
+            const uint32_t w = qraw[sd][u][e >> 1];
             x[sd][8 * u + e] = __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
             am = fmaxf(am, fabsf(x[sd][8 * u + e]));
           }
-        }
       am = fmaxf(am, __shfl_xor(am, 16));
       am = fmaxf(am, __shfl_xor(am, 32));
       // am = f 2^ex with f in [1/2, 1): scale by 2^(8 - ex)
@@ -225,9 +238,6 @@ void paged_wide_kernel(PagedArgs a) {
           qh[sd][w] = fp8x4_split(x0, x1, x2, x3, h0, h1, h2, h3);
           ql[sd][w] = fp8x4_split(x0 - h0, x1 - h1, x2 - h2, x3 - h3, l0, l1, l2, l3);
         }
-    } else {
-#pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) qf[s] = *reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g);
     }
   };
 
@@ -398,10 +408,10 @@ void paged_wide_kernel(PagedArgs a) {
 #pragma unroll
   for (int p = 0; p < NB; ++p) issue(p, kr[p], vr[p]);
   // retire the query loads (the oldest) before the loop, so that the
-  // compiler's wait counts inside it stay exact
+  // compiler's wait counts inside it stay exact (the fp8 split consumes them)
+  split_q();
 #pragma unroll
   for (int s = 0; s < (C::F8S ? 0 : C::NSTEP); ++s) asm volatile("" ::"v"(qf[s]));
-  // (the fp8 split consumes every query load inside load_q)
   if (nst > 0) put(kr[0], vr[0], tiles[0][0], tiles[0][1]);
   issue(NB, kr[0], vr[0]);
   __syncthreads();
