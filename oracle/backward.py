@@ -33,7 +33,7 @@ from typing import Sequence
 
 import numpy as np
 
-from .attention import build_kv
+from .attention import build_kv, chain_of
 from .decode import decode
 
 _ROW_CHUNK = 512
@@ -128,6 +128,74 @@ def attn_flat_bwd(q, k, v, do, prefix_len: int, seg_offsets: Sequence[int], sm_s
         lk = np.nonzero(slot_k[idx] >= 0)[0]
         gq, gk, gv = causal_attention_bwd(qx, kx, vx, dox, sm_scale, q_rows=lr, k_rows=lk)
         # each stored row appears once per expansion, so each copy adds once
+        dq[slot_r[idx[lr]]] += gq
+        dk[slot_k[idx[lk]]] += gk
+        dv[slot_k[idx[lk]]] += gv
+    return dq, dk, dv
+
+
+def attn_flat_tree_bwd(q, k, v, do, prefix_len: int, seg_offsets: Sequence[int], seg_parent: Sequence[int],
+                       sm_scale: float, dtype: int = 0, rows=None, keys=None):
+    """Gradients of the multi-level flat forward (``attn_flat_tree``).
+
+    The forward takes the prefix rows from the prefix alone and the own rows of
+    segment i from its expansion [P | ancestors, root-most first | own] (the
+    build_kv copy extended down the chain, PrefixSharing PR #50, mask
+    construction and the planned multi-level tree support).  The copies keep
+    the gradient flowing back to the stored rows (the page's key changes,
+    ``.copy_()``), so, step by step:
+
+    1. the prefix expansion [P] with the prefix rows' dO;
+    2. for each segment i, its expansion with dO on its own rows only (the
+       other rows of the expansion are copies whose outputs come from their
+       own expansions, so they receive no upstream gradient there);
+    3. the textbook causal attention backward of each expansion
+       (``causal_attention_bwd``);
+    4. every stored row collects the gradients of all its copies.
+
+    q, do: [T, Hq, D]; k, v: [T, Hkv, D], storage form ``dtype`` or float64
+    when dtype is None.  seg_parent[i] in [-1, i).  rows / keys restrict the
+    dQ rows and dK / dV rows formed.  Returns dQ, dK, dV in float64.
+    """
+    def dec(x):
+        return x if dtype is None else decode(x, dtype)
+
+    offs = [int(x) for x in seg_offsets]
+    t_n, hq, d = q.shape
+    hkv = k.shape[1]
+    p = int(prefix_len)
+    n = len(offs) - 1
+    if offs[0] != p or offs[-1] != t_n or any(b < a for a, b in zip(offs, offs[1:])):
+        raise ValueError("bad seg_offsets")
+    if any(not (-1 <= int(seg_parent[i]) < i) for i in range(n)):
+        raise ValueError("seg_parent[i] must lie in [-1, i)")
+    want_r = np.arange(t_n) if rows is None else np.asarray(rows, dtype=np.int64)
+    want_k = np.arange(t_n) if keys is None else np.asarray(keys, dtype=np.int64)
+    slot_r = np.full(t_n, -1, dtype=np.int64)
+    slot_r[want_r] = np.arange(want_r.size)
+    slot_k = np.full(t_n, -1, dtype=np.int64)
+    slot_k[want_k] = np.arange(want_k.size)
+    dq = np.zeros((want_r.size, hq, d), dtype=np.float64)
+    dk = np.zeros((want_k.size, hkv, d), dtype=np.float64)
+    dv = np.zeros((want_k.size, hkv, d), dtype=np.float64)
+    expansions = []
+    if p > 0:
+        expansions.append((np.arange(p), np.arange(p)))  # (stored rows, rows that take dO)
+    for i in range(n):
+        a, b = offs[i], offs[i + 1]
+        if b == a:
+            continue
+        idx = np.concatenate([np.arange(p)] + [np.arange(offs[j], offs[j + 1]) for j in chain_of(i, seg_parent)])
+        expansions.append((idx, np.arange(a, b)))
+    for idx, own in expansions:
+        idx = idx.astype(np.int64)
+        dox = np.zeros((idx.size, hq, d), dtype=np.float64)
+        m = idx.size
+        dox[m - own.size:] = np.asarray(dec(do[own]), dtype=np.float64)  # own rows close the expansion
+        lr = np.nonzero(slot_r[idx] >= 0)[0]
+        lk = np.nonzero(slot_k[idx] >= 0)[0]
+        gq, gk, gv = causal_attention_bwd(dec(q[idx]), dec(k[idx]), dec(v[idx]), dox, sm_scale, q_rows=lr,
+                                          k_rows=lk)
         dq[slot_r[idx[lr]]] += gq
         dk[slot_k[idx[lk]]] += gk
         dv[slot_k[idx[lk]]] += gv
