@@ -219,7 +219,7 @@ class BwdRunner:
     """The flat backward at one instance: forward outputs computed once, then
     each call runs psattn_bwd (row terms, dQ, dK/dV, conversion)."""
 
-    def __init__(self, ps, inst):
+    def __init__(self, ps, inst, seg_parent=None):
         import torch
         from gpu_util import to_dev
         from psattn_inputs import f32_to_bf16_bits
@@ -229,20 +229,22 @@ class BwdRunner:
         self.k = to_dev(inst.k, inst.dtype)
         self.v = to_dev(inst.v, inst.dtype)
         self.seg = torch.from_numpy(inst.seg_offsets).cuda()
+        self.par = None if seg_parent is None else torch.from_numpy(np.asarray(seg_parent, dtype=np.int32)).cuda()
         self.o, self.lse = ps.fwd_flat(self.q, self.k, self.v, inst.prefix_len, self.seg, inst.max_seg_len,
-                                       sm_scale=inst.sm_scale)
+                                       sm_scale=inst.sm_scale, seg_parent=self.par)
         rng = np.random.default_rng(inst.seed + 1000)
         self.do = to_dev(f32_to_bf16_bits(rng.standard_normal(inst.q.shape).astype(np.float32)), inst.dtype)
         self.dq, self.dk, self.dv = torch.empty_like(self.q), torch.empty_like(self.k), torch.empty_like(self.v)
         desc = ps.flat_desc(inst.total_tokens, inst.prefix_len, inst.num_segments, self.seg.data_ptr(),
-                            inst.max_seg_len)
+                            inst.max_seg_len, 0 if self.par is None else self.par.data_ptr())
         nb = ps.psattn_bwd_workspace_size(desc, inst.hq, inst.hkv, inst.d, inst.dtype)
         self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
 
     def __call__(self):
         i = self.inst
         self.ps.bwd_flat(self.q, self.k, self.v, self.o, self.lse, self.do, i.prefix_len, self.seg, i.max_seg_len,
-                         sm_scale=i.sm_scale, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+                         sm_scale=i.sm_scale, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws,
+                         seg_parent=self.par)
 
     def outputs(self):
         return self.dq, self.dk, self.dv
@@ -580,6 +582,18 @@ def main():
                               "parents": parents}
         recs["grpo_chain"].update(time_record(tc))
         del cr
+        # and its backward
+        log("timing grpo_chain_bwd")
+        cb = BwdRunner(ps, c_inst, seg_parent=parents)
+        if not args.no_check:
+            check_finite(cb, "grpo_chain_bwd")
+        tcb = time_calls(cb, flush, max(3, args.steps // 2), 2)
+        cbf = 2.5 * cf
+        recs["grpo_chain_bwd"] = {"useful_tflops": round(cbf / (tcb["mean"] * 1e-3) / 1e12, 2),
+                                  "frac": round(cbf / (tcb["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "parents": parents}
+        recs["grpo_chain_bwd"].update(time_record(tcb))
+        del cb
         # sparse shared-latent MLA (DSA prefill): 16384 tokens, 64 heads,
         # top-2048 lists over the prompt's own 512-wide latent rows
         log("timing mla_dsa")

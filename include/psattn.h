@@ -91,7 +91,7 @@ enum { PSATTN_MODE_FLAT = 0, PSATTN_MODE_PAGED = 1 };
  *     [P | ancestors, root-most first | S_i].  Entries outside [-1, i) end
  *     the ancestor walk there (no out-of-bounds read, no endless loop, but
  *     those rows are then wrong).  NULL: one level (every parent is -1).
- *     bf16 only, forward only; ignored in paged mode.
+ *     bf16 only (forward and psattn_bwd); ignored in paged mode.
  *
  * Paged mode (speculative target-verify; draft_len rows per request, or
  * ragged lengths through qo_indptr):
@@ -248,7 +248,9 @@ psattn_status psattn_fwd_noalloc(const void* q, const void* k, const void* v, vo
  * flat output's prefix rows count once.
  *
  * Bytes of scratch psattn_bwd needs (flat mode only): lse2 and delta, [T, Hq]
- * fp32 each, and fp32 dK / dV accumulators, [T, Hkv, D] each.  Host only.
+ * fp32 each, fp32 dK / dV accumulators, [T, Hkv, D] each, and a table of
+ * the key-major pass's work items (16 bytes each, as many as the host's bound
+ * on one kv head's items from the descriptor's scalars).  Host only.
  * Returns 0 and sets the last error on invalid or unsupported input.
  */
 size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,
@@ -261,7 +263,11 @@ size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hk
  *   lse          : the forward's LSE [T, Hq], fp32, natural log.
  *   dout         : dO [T, Hq, D], q's dtype.
  *   dq, dk, dv   : outputs, layouts of q, k, v, in q's dtype; fully written.
- *   desc         : flat descriptor (mode PSATTN_MODE_FLAT), as for psattn_fwd.
+ *   desc         : flat descriptor (mode PSATTN_MODE_FLAT), as for psattn_fwd,
+ *                  seg_parent included: with it, the gradient of the
+ *                  multi-level forward (each segment's expansion copies the
+ *                  prefix and its ancestors' tokens, and every copy's gradient
+ *                  flows back to the stored row).
  *   d            : 128.  dtype: PSATTN_BF16.  hq / hkv <= 64.
  *   sm_scale     : the forward's logit scale.
  *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,

@@ -54,7 +54,7 @@ struct PagedArgs {
 };
 
 // Backward of the flat forward (bf16).  Workspace: lse2 and delta [T, Hq]
-// fp32, acc_k and acc_v [T, Hkv, D] fp32.
+// fp32, acc_k and acc_v [T, Hkv, D] fp32, the dK/dV item table.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -69,7 +69,10 @@ struct BwdArgs {
   float* delta;  // sum_d dO O
   float* acc_k;
   float* acc_v;
+  int32_t* item_tab;  // [n_tab][4] the dK/dV items of one kv head: k0, k1, r0, r1 (k1 <= k0: none)
+  int32_t n_tab;
   const int32_t* seg_offsets;
+  const int32_t* seg_parent;  // [N] parent segment (-1: the prefix), or null: one level
   int64_t total_tokens;
   int32_t prefix_len;
   int32_t nseg;
@@ -81,8 +84,8 @@ struct BwdArgs {
   float scale_log2;     // sm_scale * log2(e)
   float sm_scale;
 };
-// pre (delta, lse2, zeroed accumulators), dQ, dK/dV and the final conversion,
-// defined in psattn_bwd.hip
+// pre (delta, lse2, zeroed accumulators, the item table), dQ, dK/dV and the
+// final conversion, defined in psattn_bwd.hip
 int launch_flat_bwd(const BwdArgs& a, int d, int64_t dq_blocks, int64_t dkdv_blocks, void* stream);
 
 // dtype codes follow psattn_dtype (0 f32, 1 bf16, 2 fp8 e4m3fn)

@@ -252,17 +252,36 @@ PS_HD Splits paged_splits(int32_t batch, int32_t hkv, int32_t max_prefix_len, in
 // most kBwdKeys, inside the prefix or inside one rollout) against the query
 // tokens [r0, r1) of one chunk (at most `rc` tokens) of a row range that sees
 // those keys.  Prefix keys are seen by the prefix rows from k0 on and by every
-// rollout's rows; a rollout's keys by that rollout's rows from k0 on.  Items
-// of one kv head, in order: the prefix key tiles, each with its prefix-row
-// chunks and then every rollout's chunks (rollouts in order); then every
-// rollout's key tiles in order, each with its own row chunks.
+// rollout's rows; a rollout's keys by that rollout's rows from k0 on, and
+// (multi-level sharing, seg_parent set) by every row of each segment that
+// descends from it.  Items of one kv head, in order: the prefix key tiles,
+// each with its prefix-row chunks and then every rollout's chunks (rollouts
+// in order); then every rollout's key tiles in order, each with its own row
+// chunks and then the chunks of its descendants (in segment order).  A
+// descendant follows its ancestors in the buffer, so its rows lie past every
+// key of the tile: the tile is wholly visible to them.
 constexpr int kBwdKeys = 128;
+
+// Segment `anc` is a proper ancestor of segment s: the walk up s's parents,
+// which ends at -1 (the prefix) or at an entry outside [-1, child), the same
+// walk as the forward's, meets it.
+PS_HD bool seg_has_ancestor(const int32_t* seg_parent, int32_t s, int32_t anc) {
+  int32_t child = s;
+  int32_t p = seg_parent[s];
+  while (p >= 0 && p < child) {
+    if (p == anc) return true;
+    child = p;
+    p = seg_parent[p];
+  }
+  return false;
+}
 
 struct BwdItem {
   int32_t valid, k0, k1, r0, r1;
 };
 
-PS_HD BwdItem dkdv_item(int32_t j, int32_t prefix_len, int32_t nseg, const int32_t* seg_offsets, int32_t rc) {
+PS_HD BwdItem dkdv_item(int32_t j, int32_t prefix_len, int32_t nseg, const int32_t* seg_offsets,
+                        const int32_t* seg_parent, int32_t rc) {
   BwdItem it{0, 0, 0, 0, 0};
   int32_t rem = j;
   int32_t sr = 0;  // chunks of all rollouts' rows
@@ -310,19 +329,36 @@ PS_HD BwdItem dkdv_item(int32_t j, int32_t prefix_len, int32_t nseg, const int32
         return it;
       }
       rem -= n;
+      if (!seg_parent) continue;
+      for (int32_t e = i + 1; e < nseg; ++e) {
+        if (!seg_has_ancestor(seg_parent, e, i)) continue;
+        const int32_t ae = seg_offsets[e], be = seg_offsets[e + 1];
+        const int32_t ne = cdiv32(be - ae, rc);
+        if (rem < ne) {
+          it.valid = 1;
+          it.k0 = k0;
+          it.k1 = imin(k0 + kBwdKeys, b);
+          it.r0 = ae + rem * rc;
+          it.r1 = imin(it.r0 + rc, be);
+          return it;
+        }
+        rem -= ne;
+      }
     }
   }
   return it;
 }
 
-// Upper bound on the dK/dV items of one kv head from host scalars only.
+// Upper bound on the dK/dV items of one kv head from host scalars only
+// (chain: multi-level sharing, where a rollout key tile also takes the
+// chunks of its descendants, at most all rollouts' chunks).
 PS_HD int64_t dkdv_items_per_head_ub(int64_t prefix_len, int64_t total, int64_t nseg, int64_t max_seg,
-                                     int64_t rc) {
+                                     int64_t rc, bool chain) {
   const int64_t suf = total - prefix_len;
   const int64_t sr = cdiv64(suf, rc) + nseg;  // >= sum_i ceil(S_i / rc)
   const int64_t pre = cdiv64(prefix_len, kBwdKeys) * (cdiv64(prefix_len, rc) + sr);
   const int64_t rtiles = suf / kBwdKeys + nseg;  // >= number of rollout key tiles
-  return pre + rtiles * cdiv64(max_seg, rc);
+  return pre + rtiles * (cdiv64(max_seg, rc) + (chain ? sr : 0));
 }
 
 // Ragged draft lengths: request b's draft rows (of q, o, lse, k_ext, v_ext)

@@ -156,7 +156,8 @@ struct BwdPlan {
   Plan base;
   int64_t dq_blocks = 0;
   int64_t dkdv_blocks = 0;
-  size_t off_delta = 0, off_acck = 0, off_accv = 0, ws_bytes = 0;
+  size_t off_delta = 0, off_acck = 0, off_accv = 0, off_items = 0, ws_bytes = 0;
+  int64_t n_tab = 0;  // dK/dV items of one kv head in the one-item launch (its table's entries)
 };
 
 psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t hd, psattn_dtype dt,
@@ -165,21 +166,22 @@ psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t h
   psattn_status st = check_common(d, hq, hkv, hd, dt, dt, &bp->base);
   if (st != PSATTN_OK) return st;
   if (dt != PSATTN_BF16) return fail(PSATTN_E_UNSUPPORTED, "the backward takes bf16 only");
-  if (d->seg_parent) return fail(PSATTN_E_UNSUPPORTED, "the backward covers one-level sharing only (seg_parent set)");
   if (hd != 128) return fail(PSATTN_E_UNSUPPORTED, "the backward takes head dim 128 only (got %d)", hd);
   if (bp->base.g > 64) return fail(PSATTN_E_UNSUPPORTED, "the backward takes GQA groups up to 64 (got %d)", bp->base.g);
   const int64_t t = d->total_tokens;
   bp->dq_blocks = bp->base.flat_blocks;
-  bp->dkdv_blocks =
-      t == 0 ? 0
-             : dkdv_items_per_head_ub(d->prefix_len, t, d->num_segments, d->max_seg_len, kBwdRowChunk) * hkv;
+  bp->n_tab = t == 0 ? 0
+                     : dkdv_items_per_head_ub(d->prefix_len, t, d->num_segments, d->max_seg_len, kBwdRowChunk,
+                                              d->num_segments > 0 && d->seg_parent != nullptr);
+  bp->dkdv_blocks = bp->n_tab * hkv;
   if (bp->dkdv_blocks > INT32_MAX) return fail(PSATTN_E_UNSUPPORTED, "grid too large");
   const size_t rows = (size_t)t * hq * sizeof(float);
   const size_t acc = (size_t)t * hkv * hd * sizeof(float);
   bp->off_delta = round_up(rows, kWsAlign);
   bp->off_acck = bp->off_delta + round_up(rows, kWsAlign);
   bp->off_accv = bp->off_acck + round_up(acc, kWsAlign);
-  bp->ws_bytes = t == 0 ? 0 : bp->off_accv + round_up(acc, kWsAlign);
+  bp->off_items = bp->off_accv + round_up(acc, kWsAlign);
+  bp->ws_bytes = t == 0 ? 0 : bp->off_items + round_up((size_t)bp->n_tab * 4 * sizeof(int32_t), kWsAlign);
   return PSATTN_OK;
 }
 
@@ -362,7 +364,10 @@ psattn_status psattn_bwd(const void* q, const void* k, const void* v, const void
   a.delta = reinterpret_cast<float*>(ws + bp.off_delta);
   a.acc_k = reinterpret_cast<float*>(ws + bp.off_acck);
   a.acc_v = reinterpret_cast<float*>(ws + bp.off_accv);
+  a.item_tab = reinterpret_cast<int32_t*>(ws + bp.off_items);
+  a.n_tab = (int32_t)bp.n_tab;
   a.seg_offsets = desc->seg_offsets;
+  a.seg_parent = desc->num_segments > 0 ? desc->seg_parent : nullptr;
   a.total_tokens = desc->total_tokens;
   a.prefix_len = desc->prefix_len;
   a.nseg = desc->num_segments;

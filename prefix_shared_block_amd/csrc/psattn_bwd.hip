@@ -62,7 +62,10 @@ struct BCfg {
 };
 
 // ------------------------------------------------------------------- dQ pass
-template <int D>
+// CHAIN: multi-level sharing (seg_parent set): after the item's own walk
+// (the prefix, then its rollout up to its tile), one pass per ancestor
+// segment walks that segment's keys, all visible (the forward's walk).
+template <int D, bool CHAIN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
@@ -105,30 +108,33 @@ void bwd_dq_kernel(BwdArgs a) {
   const float lse2 = valid ? a.lse2[qrow] : __builtin_inff();
   const float delta = valid ? a.delta[qrow] : 0.f;
 
-  const int n0 = cdiv32(it.r0_end - it.r0_begin, BN);
-  const int n1 = cdiv32(it.r1_end - it.r1_begin, BN);
-  const int nt = n0 + n1;
+  // key ranges of the current pass (CHAIN: later passes put an ancestor
+  // segment's range in r0, all of it at or before the item's first row)
+  int r0b = it.r0_begin, r0e = it.r0_end, r1b = it.r1_begin, r1e = it.r1_end;
+  int n0 = cdiv32(r0e - r0b, BN);
+  int n1 = cdiv32(r1e - r1b, BN);
+  int nt = n0 + n1;
   auto n_clean = [&](int b, int e) __attribute__((always_inline)) {
     const int whole = (e - b) / BN;
     const int causal = it.q_begin + 1 - b >= 0 ? (it.q_begin + 1 - b) / BN : 0;
     return whole < causal ? whole : causal;
   };
-  const int c0 = n0 > 0 ? n_clean(it.r0_begin, it.r0_end) : 0;
-  const int c1 = n1 > 0 ? n_clean(it.r1_begin, it.r1_end) : 0;
-  const int nc = c0 + c1;
+  int c0 = n0 > 0 ? n_clean(r0b, r0e) : 0;
+  int c1 = n1 > 0 ? n_clean(r1b, r1e) : 0;
+  int nc = c0 + c1;
   auto tile_range = [&](int n, int& k0, int& ke) __attribute__((always_inline)) {
     if (n < c0) {
-      k0 = it.r0_begin + n * BN;
-      ke = it.r0_end;
+      k0 = r0b + n * BN;
+      ke = r0e;
     } else if (n < nc) {
-      k0 = it.r1_begin + (n - c0) * BN;
-      ke = it.r1_end;
+      k0 = r1b + (n - c0) * BN;
+      ke = r1e;
     } else if (n < nc + n0 - c0) {
-      k0 = it.r0_begin + (n - c1) * BN;
-      ke = it.r0_end;
+      k0 = r0b + (n - c1) * BN;
+      ke = r0e;
     } else {
-      k0 = it.r1_begin + (n - n0) * BN;
-      ke = it.r1_end;
+      k0 = r1b + (n - n0) * BN;
+      ke = r1e;
     }
   };
 
@@ -252,20 +258,45 @@ void bwd_dq_kernel(BwdArgs a) {
   if (nt > 0) issue(0, 0);
 #pragma unroll
   for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(qf[s]), "v"(df[s]));
-  wait_vmcnt<0>();
-  __syncthreads();
-  int n = 0;
-  for (; n < nc; ++n) {
-    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    compute(n, std::false_type{});
+  int anc = CHAIN && it.kind == kFlatSuffix && a.seg_parent ? a.seg_parent[it.seg] : -1;
+  int child = it.seg;
+  for (;;) {
     wait_vmcnt<0>();
     __syncthreads();
-  }
-  for (; n < nt; ++n) {
-    if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
-    compute(n, std::true_type{});
-    wait_vmcnt<0>();
-    __syncthreads();
+    int n = 0;
+    for (; n < nc; ++n) {
+      if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+      compute(n, std::false_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    for (; n < nt; ++n) {
+      if (n + 1 < nt) issue(n + 1, (n + 1) & 1);
+      compute(n, std::true_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if constexpr (!CHAIN) {
+      break;
+    } else {
+      // the next ancestor segment.  A parent precedes its child and -1 is
+      // the prefix, already walked; an entry outside [-1, child) ends the
+      // walk, so the loop always ends and never reads outside seg_offsets.
+      anc = __builtin_amdgcn_readfirstlane(anc);
+      if (anc < 0 || anc >= child) break;
+      child = anc;
+      r0b = __builtin_amdgcn_readfirstlane(a.seg_offsets[anc]);
+      r0e = __builtin_amdgcn_readfirstlane(a.seg_offsets[anc + 1]);
+      r1b = r1e = 0;
+      anc = a.seg_parent[anc];
+      n0 = cdiv32(r0e - r0b, BN);
+      n1 = 0;
+      nt = n0;
+      c0 = n0 > 0 ? n_clean(r0b, r0e) : 0;
+      c1 = 0;
+      nc = c0;
+      if (nt > 0) issue(0, 0);
+    }
   }
 
   // dQ = sm_scale (dQ^T)^T: staged through LDS (chunk c of row r at
@@ -331,7 +362,17 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
   const int h_kv = blk % a.hkv;
   const int nper = (int)(gridDim.x / (unsigned)a.hkv);
   for (int item = first_item + blk / a.hkv;; item += nper) {
-    const BwdItem bi = dkdv_item(item, a.prefix_len, a.nseg, a.seg_offsets, a.row_chunk);
+    // the one-item launch reads its item from the table the row-terms pass
+    // wrote (one load instead of a scan over the segments, which for a
+    // segment tree took longer than many items' own work); the walking
+    // launch, past the table, enumerates
+    BwdItem bi;
+    if constexpr (!WALK) {
+      const int4 e = *reinterpret_cast<const int4*>(a.item_tab + 4 * (size_t)item);
+      bi = BwdItem{e.y > e.x ? 1 : 0, e.x, e.y, e.z, e.w};
+    } else {
+      bi = dkdv_item(item, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
+    }
     if (!bi.valid) return;
 
     const int tid = threadIdx.x;
@@ -597,10 +638,16 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
 
 // ------------------------------------------------------- pre and post passes
 // delta and lse2 for rows [T * Hq]: 16 lanes per row (8 elements each); the
-// accumulators are zeroed by the same grid
+// accumulators are zeroed and the dK/dV item table is written (thread j:
+// item j of a kv head) by the same grid
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int64_t nrows, int64_t nacc4) {
   const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gtid < a.n_tab) {
+    const BwdItem bi = dkdv_item((int32_t)gtid, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
+    const int4 e = bi.valid ? int4{bi.k0, bi.k1, bi.r0, bi.r1} : int4{0, 0, 0, 0};
+    *reinterpret_cast<int4*>(a.item_tab + 4 * gtid) = e;
+  }
   const int64_t row = gtid / (D / 8);
   const int part = (int)(gtid % (D / 8));
   float s = 0.f;
@@ -653,14 +700,17 @@ template <int D>
 int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipStream_t s) {
   const int64_t nrows = a.total_tokens * a.hq;
   const int64_t nacc4 = a.total_tokens * a.hkv * D / 4;
-  const int64_t pre_threads = nrows * (D / 8);
+  const int64_t pre_threads = nrows * (D / 8) > a.n_tab ? nrows * (D / 8) : a.n_tab;
   int64_t pre_blocks = (pre_threads + 255) / 256;
   if (pre_blocks < 1) pre_blocks = 1;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, s, a, nrows, nacc4);
   int err = (int)hipGetLastError();
   if (err) return err;
   if (dq_blocks > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
+    if (a.seg_parent)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
     if ((err = (int)hipGetLastError())) return err;
   }
   if (dkdv_blocks > 0) {

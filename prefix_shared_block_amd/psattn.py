@@ -260,10 +260,10 @@ def fwd_flat(q, k, v, prefix_len: int, seg_offsets, max_seg_len: int, sm_scale: 
 
 
 def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: int,
-             sm_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None):
+             sm_scale: Optional[float] = None, dq=None, dk=None, dv=None, workspace=None, seg_parent=None):
     """Gradients of the flat forward for the upstream gradient dout.  o and
-    lse are the forward's outputs; shapes and the descriptor as in fwd_flat.
-    Returns (dq, dk, dv)."""
+    lse are the forward's outputs; shapes and the descriptor (seg_parent
+    included) as in fwd_flat.  Returns (dq, dk, dv)."""
     import torch
 
     t_n, hq, d = q.shape
@@ -274,7 +274,9 @@ def bwd_flat(q, k, v, o, lse, dout, prefix_len: int, seg_offsets, max_seg_len: i
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     n = int(seg_offsets.numel()) - 1 if seg_offsets is not None else 0
-    desc = flat_desc(t_n, prefix_len, n, _ptr(seg_offsets), max_seg_len)
+    if seg_parent is not None and int(seg_parent.numel()) != n:
+        raise ValueError(f"seg_parent has {int(seg_parent.numel())} entries, {n} segments")
+    desc = flat_desc(t_n, prefix_len, n, _ptr(seg_offsets), max_seg_len, _ptr(seg_parent))
     dt = _dtype_code(q)
     ws_bytes = psattn_bwd_workspace_size(desc, hq, hkv, d, dt)
     if ws_bytes == 0 and t_n > 0:

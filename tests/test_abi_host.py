@@ -99,13 +99,17 @@ def test_flat_descriptor_validation(lib, desc_kw, status):
     assert _call(_flat(**desc_kw)) == status
 
 
-def test_seg_parent_takes_bf16_forward_only(lib):
-    # multi-level sharing: the bf16 kernel only; fp32 and the backward refuse it
+def test_seg_parent_takes_bf16_only(lib):
+    # multi-level sharing: the bf16 kernels only; the fp32 forward refuses it,
+    # the bf16 backward takes it with the one-level workspace (its scratch
+    # does not depend on the tree)
     d = ps.flat_desc(96, 64, 2, FAKE, 16, seg_parent_ptr=FAKE)
     assert _call(d, qdt=ps.F32, kvdt=ps.F32) == ps.E_UNSUPPORTED
     assert "seg_parent" in ps.psattn_last_error()
-    assert _bwd(d) == ps.E_UNSUPPORTED
-    assert "seg_parent" in ps.psattn_last_error()
+    one = ps.flat_desc(96, 64, 2, FAKE, 16)
+    assert ps.psattn_bwd_workspace_size(d, 8, 2, 128, ps.BF16) == ps.psattn_bwd_workspace_size(one, 8, 2, 128,
+                                                                                               ps.BF16) > 0
+    assert _bwd(d, dt=ps.F32) == ps.E_UNSUPPORTED
 
 
 def test_flat_gqa_group_too_large(lib):
@@ -270,10 +274,14 @@ def test_bwd_paged_mode_unsupported(lib):
 
 
 def test_bwd_workspace_size(lib):
-    # lse2 and delta [T, Hq] fp32, then the dK / dV accumulators [T, Hkv, D] fp32, each 256-byte aligned
+    # lse2 and delta [T, Hq] fp32, then the dK / dV accumulators [T, Hkv, D] fp32, then the table of
+    # one kv head's dK/dV items (16 bytes each), each 256-byte aligned.  Items: P = 64, two
+    # rollouts of 32 tokens, max_seg_len 16: one prefix key tile with one prefix chunk and
+    # 32 / 512 + 2 rollout chunks (bound), and 32 / 128 + 2 rollout key tiles with one chunk each
     t, hq, hkv, d = 96, 8, 2, 128
     up = lambda x: (x + 255) // 256 * 256
-    want = 2 * up(t * hq * 4) + 2 * up(t * hkv * d * 4)
+    n_items = 1 * (1 + (0 + 2)) + (0 + 2) * 1
+    want = 2 * up(t * hq * 4) + 2 * up(t * hkv * d * 4) + up(16 * n_items)
     assert ps.psattn_bwd_workspace_size(_flat(t=t, p=64, n=2, mx=16), hq, hkv, d, ps.BF16) == want
     assert ps.psattn_bwd_workspace_size(ps.flat_desc(0, 0, 0, 0, 0), hq, hkv, d, ps.BF16) == 0
 
