@@ -52,13 +52,20 @@ template <int D>
 struct BCfg {
   static constexpr int ROWB = 2 * D;       // bytes of a bf16 row
   static constexpr int CPR = ROWB / 16;    // 16-byte chunks per row
+  static constexpr int RPK = 1024 / ROWB;  // rows per 1 KiB copy block
   static constexpr int NSTEP = D / 16;     // k-steps over the head dimension
   static constexpr int NDB = D / 32;       // 32-column blocks of the head dimension
-  static_assert(CPR == 16, "the two-way swizzle assumes 16 chunks per row");
-  // rows read both ways
-  __device__ static constexpr int fb(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-  // rows read by rows only
-  __device__ static constexpr int fk(int r) { return r & (CPR - 1); }
+  static_assert(CPR == 16 || CPR == 8, "head dims 128 and 64");
+  // Rows read both ways.  256-byte rows (D = 128): c ^ (4 (r & 3) + (r >> 2 & 3))
+  // as described above.  128-byte rows (D = 64) put two rows in one 256-byte
+  // bank row, so (row parity, slot) must differ across a pass: slot
+  // c ^ (2 (r >> 1 & 3) + (r >> 3 & 1)) does it for the 16-row pass and for the
+  // 4-row x 4-half-chunk transposed pass (checked exhaustively on the host).
+  __device__ static constexpr int fb(int r) {
+    return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+  }
+  // rows read by rows only (with 128-byte rows, by the row pair)
+  __device__ static constexpr int fk(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // ------------------------------------------------------------------- dQ pass
@@ -146,14 +153,24 @@ void bwd_dq_kernel(BwdArgs a) {
   // K is read by rows and transposed (swizzle fb), V by rows only (fk)
   auto swz = [&](int row) __attribute__((always_inline)) { return w_isv ? C::fk(row) : C::fb(row); };
   // Copy t of this wave is 1 KiB block jb = (wave CPW + t) mod NCOPY: rows
-  // 4 jb .. 4 jb + 3 (the row part of the source offset goes to the scalar
-  // base), lane l on row 4 jb + l / 16, chunk l % 16.  With 16 chunks per row
-  // both swizzles reduce to copy 0's lane offset with bits flipped by t & 3:
-  // bits 4..5 for fb (K), bits 6..7 for fk (V).
-  static_assert(C::CPR == 16 && CPW % 4 == 0, "copy offsets repeat with period 4");
+  // RPK jb .. RPK jb + RPK - 1 (the row part of the source offset goes to the
+  // scalar base), lane l on row RPK jb + l / CPR, chunk l % CPR.  With 16
+  // chunks per row both swizzles reduce to copy 0's lane offset with bits
+  // flipped by t & 3: bits 4..5 for fb (K), bits 6..7 for fk (V); with 8,
+  // each copy keeps its own offset.
+  static_assert(C::CPR != 16 || CPW % 4 == 0, "copy offsets repeat with period 4");
   const uint32_t coff0 = (uint32_t)(lane / C::CPR) * row_stride +
-                         16u * (uint32_t)((lane % C::CPR) ^ swz(4 * ((wave * CPW) % NCOPY) + lane / C::CPR));
+                         16u * (uint32_t)((lane % C::CPR) ^ swz(C::RPK * ((wave * CPW) % NCOPY) + lane / C::CPR));
   const uint32_t cflip = w_isv ? 64u : 16u;
+  uint32_t coffs[C::CPR == 16 ? 1 : CPW];
+  if constexpr (C::CPR != 16) {
+#pragma unroll
+    for (int t = 0; t < CPW; ++t) {
+      const int jb = (wave * CPW + t) % NCOPY;
+      coffs[t] = (uint32_t)(lane / C::CPR) * row_stride +
+                 16u * (uint32_t)((lane % C::CPR) ^ swz(C::RPK * jb + lane / C::CPR));
+    }
+  }
   auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
     const uint32_t bofs = (uint32_t)bsel * (2 * TILE);
     int k0, ke;
@@ -163,8 +180,8 @@ void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < CPW; ++t) {
         const int jb = (wave * CPW + t) % NCOPY;
-        dma16_s(base + (size_t)(4 * jb) * row_stride, coff0 ^ (cflip * (uint32_t)(t & 3)),
-                lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
+        const uint32_t off = C::CPR == 16 ? coff0 ^ (cflip * (uint32_t)(t & 3)) : coffs[C::CPR == 16 ? 0 : t];
+        dma16_s(base + (size_t)(C::RPK * jb) * row_stride, off, lds_addr(&smem[0][w_isv ? 1 : 0][jb * 1024]) + bofs);
       }
     } else {
       const int lastr = ke - 1 - k0;
@@ -422,7 +439,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
     };
 
     // copies: waves 0, 1 copy the Q tile, waves 2, 3 the dO tile; copy t of a
-    // wave is 1 KiB block jb, lane l on stacked row s = 4 jb + l / 16, chunk l % 16
+    // wave is 1 KiB block jb, lane l on stacked row s = RPK jb + l / CPR, chunk l % CPR
     const bool w_isd = wave * CPW >= NCOPY;
     const char* src = reinterpret_cast<const char*>(w_isd ? a.dout : a.q);
     const uint32_t tok_stride = (uint32_t)a.hq * C::ROWB;
@@ -430,7 +447,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
   #pragma unroll
     for (int t = 0; t < CPW; ++t) {
       const int jb = (wave * CPW + t) % NCOPY;
-      const int s = jb * 4 + lane / C::CPR;
+      const int s = jb * C::RPK + lane / C::CPR;
       const int pos = lane % C::CPR;
       const int sc_ = s < vrows_full ? s : vrows_full - 1;
       coff[t] = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB + 16u * (uint32_t)(pos ^ C::fb(s));
@@ -455,7 +472,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
   #pragma unroll
         for (int t = 0; t < CPW; ++t) {
           const int jb = (wave * CPW + t) % NCOPY;
-          const int s = jb * 4 + lane / C::CPR;
+          const int s = jb * C::RPK + lane / C::CPR;
           const int pos = lane % C::CPR;
           const int sc_ = s < nv ? s : nv - 1;
           const uint32_t off = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB +
@@ -603,8 +620,10 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
 
     // Add the item's partial dK^T / dV^T into the fp32 accumulators.  Each wave
     // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
-    // c ^ kr), then adds it with consecutive lanes on consecutive floats.
+    // c ^ (kr mod the row's chunks)), then adds it with consecutive lanes on
+    // consecutive floats.
     constexpr int SROW = D * 4;
+    constexpr int SMASK = SROW / 16 - 1;
     static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
     char* st = &smem[0][0][0] + wave * (32 * SROW);
   #pragma unroll
@@ -616,7 +635,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
           // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
           const f32x4_t x = which == 0 ? f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]}
                                        : f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
-          *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ l32)) = x;
+          *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ (l32 & SMASK))) = x;
         }
       __syncthreads();
       float* acc = which == 0 ? a.acc_v : a.acc_k;
@@ -626,7 +645,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
         const int f = p % D;
         const int kk = bi.k0 + 32 * wave + kr;
         if (kk < bi.k1) {
-          const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ kr) + 4 * (f & 3));
+          const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ (kr & SMASK)) + 4 * (f & 3));
           unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + f, x);
         }
       }
@@ -736,6 +755,7 @@ int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipSt
 int launch_flat_bwd(const BwdArgs& a, int d, int64_t dq_blocks, int64_t dkdv_blocks, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d == 128) return launch_bwd_t<128>(a, dq_blocks, dkdv_blocks, s);
+  if (d == 64) return launch_bwd_t<64>(a, dq_blocks, dkdv_blocks, s);
   return (int)hipErrorInvalidValue;
 }
 

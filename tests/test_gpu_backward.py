@@ -96,6 +96,18 @@ def test_bwd_small_full(gpu_lib, p, lens, hq, hkv):
     _check(gpu_lib, inst, label=f"P={p} lens={lens} hq={hq} hkv={hkv}")
 
 
+@pytest.mark.parametrize("p,lens,hq,hkv", [
+    (100, [37], 8, 2),              # N = 1
+    (0, [33, 5, 70], 8, 2),         # no prefix
+    (130, [3, 200], 12, 4),         # G = 3: every row tile masked
+    (600, [700, 513], 8, 2),        # rows of a key tile span several 512-token chunks
+    (300, [200, 128, 1, 77], 32, 8),  # GRPO head layout, small
+])
+def test_bwd_head_dim_64(gpu_lib, p, lens, hq, hkv):
+    inst = make_flat(p, lens, hq, hkv, 64, dtype=BF16, seed=p + len(lens) + hq + 64)
+    _check(gpu_lib, inst, label=f"D=64 P={p} lens={lens} hq={hq} hkv={hkv}")
+
+
 def test_bwd_grpo_block(gpu_lib):
     # the GRPO head layout at a quarter of its length
     inst = make_flat(512, [128] * 8, 32, 8, 128, dtype=BF16, seed=41, name="grpo_quarter")

@@ -95,6 +95,11 @@ def test_tree_bwd_seeded_forest(gpu_lib, seed):
     _check(gpu_lib, inst, parents, f"forest seed={seed} parents={parents.tolist()}")
 
 
+def test_tree_bwd_head_dim_64(gpu_lib):
+    inst = make_flat(90, [33, 65, 70, 20], 8, 2, 64, dtype=BF16, seed=64)
+    _check(gpu_lib, inst, [-1, 0, 1, 0], "D=64 chain")
+
+
 def test_tree_bwd_all_roots_is_one_level(gpu_lib):
     inst = make_flat(200, [90, 140, 33], 16, 4, 128, dtype=BF16, seed=5)
     _check(gpu_lib, inst, [-1, -1, -1], "all roots")
