@@ -268,7 +268,7 @@ size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hk
  *                  multi-level forward (each segment's expansion copies the
  *                  prefix and its ancestors' tokens, and every copy's gradient
  *                  flows back to the stored row).
- *   d            : 128.  dtype: PSATTN_BF16.  hq / hkv <= 64.
+ *   d            : 64 or 128.  dtype: PSATTN_BF16.  hq / hkv <= 64.
  *   sm_scale     : the forward's logit scale.
  *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,
  *                  256-byte aligned; its contents on entry do not matter.
