@@ -64,3 +64,37 @@ def mla_sparse(q, ckv, indices, sm_scale: float, sink=None, dtype: Optional[int]
         o[n] = (e[:, :keys.size] @ cs) / den[:, None]
         lse[n] = m + np.log(den)
     return o, lse
+
+
+def mla_dense(q, ckv, sm_scale: float, sink=None, dtype: Optional[int] = 1,
+              tokens: Optional[Sequence[int]] = None):
+    """Dense causal shared-latent MLA prefill (the same head-stacked latent
+    attention with every earlier cached row listed): the T query tokens are
+    the last T positions of the S-row cache, so token t sits at row
+    S - T + t and attends to rows 0 .. S - T + t (ordinary causal attention
+    with one latent row as key and value for every head).  Steps 3-5 as in
+    ``mla_sparse``.  q: [T, H, D], ckv: [S, D] (S >= T); returns o [n, H, D]
+    and lse [n, H] in float64."""
+    def dec(x):
+        return np.asarray(x, dtype=np.float64) if dtype is None else decode(x, dtype)
+
+    t_n, hq, d = q.shape
+    s_n = ckv.shape[0]
+    if s_n < t_n:
+        raise ValueError("the cache must hold the query tokens (S >= T)")
+    sel_t = np.arange(t_n) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    c = dec(ckv)
+    sk = None if sink is None else np.asarray(sink, dtype=np.float64)
+    o = np.zeros((sel_t.size, hq, d), dtype=np.float64)
+    lse = np.full((sel_t.size, hq), -np.inf, dtype=np.float64)
+    for n, t in enumerate(sel_t):
+        cs = c[: s_n - t_n + int(t) + 1]                 # rows 0 .. S - T + t
+        z = (dec(q[t]) @ cs.T) * sm_scale                # [H, rows]
+        if sk is not None:
+            z = np.concatenate([z, sk[:, None]], axis=1)
+        m = z.max(axis=1)
+        e = np.exp(z - m[:, None])
+        den = e.sum(axis=1)
+        o[n] = (e[:, : cs.shape[0]] @ cs) / den[:, None]
+        lse[n] = m + np.log(den)
+    return o, lse
