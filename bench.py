@@ -185,23 +185,33 @@ class PagedRunner:
 
 
 class MlaRunner:
-    """The sparse shared-latent MLA forward at one instance."""
+    """The shared-latent MLA forward at one instance: the sparse top-k form,
+    or with dense=True the causal prefill over the whole cache (the index
+    lists unused)."""
 
-    def __init__(self, ps, inst):
+    def __init__(self, ps, inst, dense=False):
         import torch
 
-        self.ps, self.inst = ps, inst
+        self.ps, self.inst, self.dense = ps, inst, dense
         self.q = torch.from_numpy(inst.q.view(np.int16)).view(torch.bfloat16).cuda()
         self.ckv = torch.from_numpy(inst.ckv.view(np.int16)).view(torch.bfloat16).cuda()
         self.idx = torch.from_numpy(inst.indices).cuda()
         self.sink = None if inst.sink is None else torch.from_numpy(inst.sink.astype(np.float32)).cuda()
         self.o = torch.empty_like(self.q)
         self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
-        self.n_keys = int(((inst.indices >= 0) & (inst.indices < inst.ckv.shape[0])).sum())
+        if dense:
+            t_n, s_n = inst.q.shape[0], inst.ckv.shape[0]
+            self.n_keys = sum(s_n - t_n + t + 1 for t in range(t_n))
+        else:
+            self.n_keys = int(((inst.indices >= 0) & (inst.indices < inst.ckv.shape[0])).sum())
 
     def __call__(self):
-        self.ps.fwd_mla(self.q, self.ckv, self.idx, sm_scale=self.inst.sm_scale, sink=self.sink, out=self.o,
-                        lse=self.lse)
+        if self.dense:
+            self.ps.fwd_mla_dense(self.q, self.ckv, sm_scale=self.inst.sm_scale, sink=self.sink, out=self.o,
+                                  lse=self.lse)
+        else:
+            self.ps.fwd_mla(self.q, self.ckv, self.idx, sm_scale=self.inst.sm_scale, sink=self.sink, out=self.o,
+                            lse=self.lse)
 
     def outputs(self):
         return self.o, self.lse
@@ -566,34 +576,37 @@ def main():
         recs["grpo_bwd"].update(time_record(tb))
         del gb
 
-    if args.all:
+    if args.all and (want("grpo_chain") or want("grpo_chain_bwd")):
         # multi-level sharing at the GRPO shape: two shared 512-token
         # continuations of the prompt, each continued by three rollouts
-        log("timing grpo_chain")
         c_inst = make_flat(2048, [512] * 8, 32, 8, 128, dtype=BF16, seed=77, name="grpo_chain")
         parents = [-1, -1, 0, 0, 0, 1, 1, 1]
-        cr = FlatRunner(ps, c_inst, seg_parent=parents)
-        if not args.no_check:
-            check_finite(cr, "grpo_chain")
-        tc = time_calls(cr, flush, args.steps, args.warmup)
         cf = flat_tree_useful_flops(c_inst, parents)
-        recs["grpo_chain"] = {"useful_tflops": round(cf / (tc["mean"] * 1e-3) / 1e12, 2),
-                              "frac": round(cf / (tc["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                              "parents": parents}
-        recs["grpo_chain"].update(time_record(tc))
-        del cr
-        # and its backward
-        log("timing grpo_chain_bwd")
-        cb = BwdRunner(ps, c_inst, seg_parent=parents)
-        if not args.no_check:
-            check_finite(cb, "grpo_chain_bwd")
-        tcb = time_calls(cb, flush, max(3, args.steps // 2), 2)
-        cbf = 2.5 * cf
-        recs["grpo_chain_bwd"] = {"useful_tflops": round(cbf / (tcb["mean"] * 1e-3) / 1e12, 2),
-                                  "frac": round(cbf / (tcb["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        if want("grpo_chain"):
+            log("timing grpo_chain")
+            cr = FlatRunner(ps, c_inst, seg_parent=parents)
+            if not args.no_check:
+                check_finite(cr, "grpo_chain")
+            tc = time_calls(cr, flush, args.steps, args.warmup)
+            recs["grpo_chain"] = {"useful_tflops": round(cf / (tc["mean"] * 1e-3) / 1e12, 2),
+                                  "frac": round(cf / (tc["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                   "parents": parents}
-        recs["grpo_chain_bwd"].update(time_record(tcb))
-        del cb
+            recs["grpo_chain"].update(time_record(tc))
+            del cr
+        if want("grpo_chain_bwd"):
+            # and its backward
+            log("timing grpo_chain_bwd")
+            cb = BwdRunner(ps, c_inst, seg_parent=parents)
+            if not args.no_check:
+                check_finite(cb, "grpo_chain_bwd")
+            tcb = time_calls(cb, flush, max(3, args.steps // 2), 2)
+            cbf = 2.5 * cf
+            recs["grpo_chain_bwd"] = {"useful_tflops": round(cbf / (tcb["mean"] * 1e-3) / 1e12, 2),
+                                      "frac": round(cbf / (tcb["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                      "parents": parents}
+            recs["grpo_chain_bwd"].update(time_record(tcb))
+            del cb
+    if args.all and want("mla_dsa"):
         # sparse shared-latent MLA (DSA prefill): 16384 tokens, 64 heads,
         # top-2048 lists over the prompt's own 512-wide latent rows
         log("timing mla_dsa")
@@ -607,6 +620,20 @@ def main():
                            "gathered_gbs": round(mb / (tm["mean"] * 1e-3) / 1e9, 1)}
         recs["mla_dsa"].update(time_record(tm, "ms"))
         del mr
+    if args.all and want("mla_dense"):
+        # the dense causal form: a 4096-token prefill over its own latent
+        # rows, 64 heads
+        log("timing mla_dense")
+        from psattn_inputs import make_mla
+        md = MlaRunner(ps, make_mla(4096, 64, 512, 1, seed=11, num_kv=4096, name="mla_dense"), dense=True)
+        if not args.no_check:
+            check_finite(md, "mla_dense")
+        tmd = time_calls(md, flush, max(5, args.steps // 3), 2)
+        mdf = md.useful_flops()
+        recs["mla_dense"] = {"useful_tflops": round(mdf / (tmd["mean"] * 1e-3) / 1e12, 2),
+                             "frac": round(mdf / (tmd["mean"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        recs["mla_dense"].update(time_record(tmd, "ms"))
+        del md
 
     copy_calib = copy_calibration() if args.copy_calib else None
 

@@ -316,6 +316,20 @@ psattn_status psattn_mla_fwd(const void* q, const void* ckv, const int32_t* indi
                              int32_t kv_stride, int32_t topk, float sm_scale, psattn_dtype dtype, void* stream);
 
 /*
+ * Dense causal shared-latent MLA prefill: the same head-stacked latent
+ * attention with no list (the shared-latent MLA of that page with every
+ * earlier cached row visible).  The num_tokens query tokens are the last
+ * num_tokens rows of the cache: token t sits at row num_kv - num_tokens + t
+ * and attends to rows 0 .. num_kv - num_tokens + t, in order.  Arguments,
+ * layouts, sink, outputs and limits as for psattn_mla_fwd without indices
+ * and topk; num_kv >= num_tokens (else PSATTN_E_INVAL).  Allocates nothing;
+ * one launch on `stream`.
+ */
+psattn_status psattn_mla_dense_fwd(const void* q, const void* ckv, const float* sink, void* o, float* lse,
+                                   int64_t num_tokens, int32_t num_heads, int32_t dim, int64_t num_kv,
+                                   int32_t kv_stride, float sm_scale, psattn_dtype dtype, void* stream);
+
+/*
  * Test hook: run the segment planner ON THE DEVICE for every workgroup of the
  * prefix-pass launch psattn_fwd would make and write its work items (the
  * PrefixSharing PR #50 page, "设计简介", proposes describing the visibility

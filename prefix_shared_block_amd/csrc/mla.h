@@ -1,5 +1,5 @@
-// mla.h -- internal interface of the sparse shared-latent MLA forward.  Not
-// part of the public ABI.
+// mla.h -- internal interface of the shared-latent MLA forward (sparse top-k
+// lists or dense causal).  Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -13,7 +13,7 @@ constexpr int kMlaMaxTopk = 2048;   // index entries per token staged in LDS
 struct MlaArgs {
   const void* q;           // [T, H, 512] bf16
   const void* ckv;         // [S] rows of kv_stride bf16, the first 512 used
-  const int32_t* indices;  // [T, topk]
+  const int32_t* indices;  // [T, topk], or null (dense)
   const float* sink;       // [H] natural-log sink logits, or null
   void* o;                 // [T, H, 512] bf16
   float* lse;              // [T, H] fp32, natural log
@@ -25,6 +25,7 @@ struct MlaArgs {
   float scale_log2;        // sm_scale * log2(e)
 };
 
-int launch_mla_sparse(const MlaArgs& a, void* stream);
+// dense: no list (indices null); token t takes cache rows 0 .. num_kv - num_tokens + t
+int launch_mla(const MlaArgs& a, bool dense, void* stream);
 
 }  // namespace psattn

@@ -27,7 +27,10 @@
 //    v_mfma_f32_32x32x16_bf16, reading only its dims of the tile.  So the
 //    accumulators are split by dims and the query fragments by heads: each
 //    wave holds 128 accumulator and 64 fragment registers whatever H is;
-//  * the optional per-head sink logit joins the normaliser in the epilogue.
+//  * the optional per-head sink logit joins the normaliser in the epilogue;
+//  * dense causal variant (no list): the query tokens are the cache's last
+//    rows and token t takes rows 0 .. S - T + t, in order, with the same
+//    tiles, gathers and products.
 #include "device_common.h"
 #include "mla.h"
 
@@ -67,7 +70,9 @@ __device__ __forceinline__ int pos_of(int k) { return (k >> 2) + 4 * ((k >> 1) &
 
 // NW = H / 16 waves.  Wave w: score heads 16 w .. +15; value dims
 // DW w .. DW (w + 1) with DW = 512 / NW, for head blocks 0 .. HB - 1.
-template <int NW>
+// DENSE: no list; the tokens are the cache's last rows and token t takes
+// rows 0 .. num_kv - num_tokens + t in order (a causal prefill).
+template <int NW, bool DENSE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void mla_sparse_kernel(MlaArgs a) {
   constexpr int H = 16 * NW;
@@ -105,42 +110,46 @@ void mla_sparse_kernel(MlaArgs a) {
     for (int s = 0; s < kNStep; ++s)
       qf[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(qp + 32 * s + 8 * g4));
   }
-  // the list: thread tid holds entries tid + NT r
-  int ent[PER];
-  {
-    const int32_t* ip = a.indices + (size_t)t * a.topk;
-    const int elast = a.topk > 0 ? a.topk - 1 : 0;
+  int cnt = 0;
+  if constexpr (DENSE) {
+    cnt = a.num_kv - a.num_tokens + t + 1;
+  } else {
+    // the list: thread tid holds entries tid + NT r
+    int ent[PER];
+    {
+      const int32_t* ip = a.indices + (size_t)t * a.topk;
+      const int elast = a.topk > 0 ? a.topk - 1 : 0;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) {
+        const int e = tid + NT * r;
+        const int v = a.topk > 0 ? ip[e < elast ? e : elast] : -1;
+        ent[r] = e < a.topk ? v : -1;
+      }
+    }
+    // compaction, in list order: round r places the valid entries of
+    // tid + NT r after those of the earlier rounds and lower threads
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int e = tid + NT * r;
-      const int v = a.topk > 0 ? ip[e < elast ? e : elast] : -1;
-      ent[r] = e < a.topk ? v : -1;
-    }
-  }
-  // compaction, in list order: round r places the valid entries of
-  // tid + NT r after those of the earlier rounds and lower threads
-  int cnt = 0;
+      const bool ok = (unsigned)ent[r] < (unsigned)a.num_kv;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (lane == 0) wcnt[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int before = cnt, total = cnt;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const bool ok = (unsigned)ent[r] < (unsigned)a.num_kv;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
-    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-    if (lane == 0) wcnt[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int before = cnt, total = cnt;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int cw = wcnt[w];
-      before += w < wave ? cw : 0;
-      total += cw;
+      for (int w = 0; w < NW; ++w) {
+        const int cw = wcnt[w];
+        before += w < wave ? cw : 0;
+        total += cw;
+      }
+      if (ok) sidx[before + below] = ent[r];
+      cnt = __builtin_amdgcn_readfirstlane(total);
+      __syncthreads();
     }
-    if (ok) sidx[before + below] = ent[r];
-    cnt = __builtin_amdgcn_readfirstlane(total);
-    __syncthreads();
   }
   const int ntile = (cnt + kBN - 1) / kBN;
   const int nfull = cnt / kBN;
-  const int last_id = cnt > 0 ? __builtin_amdgcn_readfirstlane(sidx[cnt - 1]) : 0;
+  const int last_id = DENSE ? cnt - 1 : (cnt > 0 ? __builtin_amdgcn_readfirstlane(sidx[cnt - 1]) : 0);
 
   const char* cbase = reinterpret_cast<const char*>(a.ckv);
   const size_t rstride = (size_t)a.kv_stride * 2;
@@ -151,7 +160,7 @@ void mla_sparse_kernel(MlaArgs a) {
     const int k0 = n * kBN + wave * RPW;
     int ids[RPW];
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) ids[i] = sidx[k0 + i];
+    for (int i = 0; i < RPW; ++i) ids[i] = DENSE ? k0 + i : sidx[k0 + i];
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = wave * RPW + i;
@@ -355,19 +364,23 @@ void mla_sparse_kernel(MlaArgs a) {
 }
 
 template <int NW>
-int launch_w(const MlaArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((mla_sparse_kernel<NW>), dim3((unsigned)a.num_tokens), dim3(64 * NW), 0, s, a);
+int launch_w(const MlaArgs& a, bool dense, hipStream_t s) {
+  if (dense)
+    hipLaunchKernelGGL((mla_sparse_kernel<NW, true>), dim3((unsigned)a.num_tokens), dim3(64 * NW), 0, s, a);
+  else
+    hipLaunchKernelGGL((mla_sparse_kernel<NW, false>), dim3((unsigned)a.num_tokens), dim3(64 * NW), 0, s, a);
   return (int)hipGetLastError();
 }
 
 }  // namespace
 
-int launch_mla_sparse(const MlaArgs& a, void* stream) {
+int launch_mla(const MlaArgs& a, bool dense, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dense && (a.num_kv < a.num_tokens || a.indices)) return (int)hipErrorInvalidValue;
   switch (a.num_heads) {
-    case 32: return launch_w<2>(a, s);
-    case 64: return launch_w<4>(a, s);
-    case 128: return launch_w<8>(a, s);
+    case 32: return launch_w<2>(a, dense, s);
+    case 64: return launch_w<4>(a, dense, s);
+    case 128: return launch_w<8>(a, dense, s);
   }
   return (int)hipErrorInvalidValue;
 }

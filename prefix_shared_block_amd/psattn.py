@@ -6,9 +6,12 @@ current HIP stream.  There is no fallback: if the library is missing or a call
 fails, an exception is raised.
 
 The C entry points are exposed under their own names (``psattn_fwd``,
-``psattn_fwd_noalloc``, ``psattn_workspace_size``, ``psattn_plan_dump``, ``psattn_plan_host``,
-``psattn_status_string``, ``psattn_last_error``) taking raw integers /
-pointers, plus two tensor-level helpers ``fwd_flat`` and ``fwd_paged``.
+``psattn_fwd_noalloc``, ``psattn_workspace_size``, ``psattn_bwd``,
+``psattn_bwd_workspace_size``, ``psattn_mla_fwd``, ``psattn_mla_dense_fwd``,
+``psattn_plan_dump``, ``psattn_plan_host``, ``psattn_status_string``,
+``psattn_last_error``) taking raw integers / pointers, plus tensor-level
+helpers (``fwd_flat``, ``fwd_paged``, ``bwd_flat``, ``fwd_mla``,
+``fwd_mla_dense``).
 """
 from __future__ import annotations
 
@@ -99,6 +102,8 @@ def load(path: Optional[str] = None):
     lib.psattn_bwd.restype = i32
     lib.psattn_mla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, i32, f32, i32, vp]
     lib.psattn_mla_fwd.restype = i32
+    lib.psattn_mla_dense_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, f32, i32, vp]
+    lib.psattn_mla_dense_fwd.restype = i32
     lib.psattn_status_string.argtypes = [i32]
     lib.psattn_status_string.restype = ctypes.c_char_p
     lib.psattn_last_error.argtypes = []
@@ -153,6 +158,12 @@ def psattn_mla_fwd(q: int, ckv: int, indices: int, sink: int, o: int, lse: int, 
                    dim: int, num_kv: int, kv_stride: int, topk: int, sm_scale: float, dtype: int, stream: int) -> int:
     return int(load().psattn_mla_fwd(q, ckv, indices, sink, o, lse, num_tokens, num_heads, dim, num_kv, kv_stride,
                                      topk, sm_scale, dtype, stream))
+
+
+def psattn_mla_dense_fwd(q: int, ckv: int, sink: int, o: int, lse: int, num_tokens: int, num_heads: int,
+                         dim: int, num_kv: int, kv_stride: int, sm_scale: float, dtype: int, stream: int) -> int:
+    return int(load().psattn_mla_dense_fwd(q, ckv, sink, o, lse, num_tokens, num_heads, dim, num_kv, kv_stride,
+                                           sm_scale, dtype, stream))
 
 
 def psattn_plan_dump(desc: PsattnDesc, hq: int, hkv: int, d: int, q_dtype: int, kv_dtype: int,
@@ -316,6 +327,31 @@ def fwd_mla(q, ckv, indices, sm_scale: Optional[float] = None, sink=None, out=No
     st = psattn_mla_fwd(_ptr(q), _ptr(ckv), _ptr(indices), _ptr(sink), _ptr(out), _ptr(lse), t_n, hq, d,
                         int(ckv.shape[0]), int(ckv.stride(0)), int(indices.shape[1]), float(sm_scale),
                         _dtype_code(q), _stream_handle(q.device))
+    check(st)
+    return out, lse
+
+
+def fwd_mla_dense(q, ckv, sm_scale: Optional[float] = None, sink=None, out=None, lse=None):
+    """Dense causal shared-latent MLA prefill.  q [T, H, 512] bf16 are the
+    last T rows of the cache ckv [S, stride] bf16 (S >= T); token t attends
+    to rows 0 .. S - T + t.  sink: optional fp32 [H].  Returns (o, lse)."""
+    import torch
+
+    t_n, hq, d = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if ckv.dim() != 2 or ckv.stride(1) != 1:
+        raise ValueError("ckv must be [S, stride] with unit column stride")
+    if not q.is_contiguous():
+        raise ValueError("q must be a contiguous [T, H, D] tensor")
+    if sink is not None and (sink.dtype != torch.float32 or sink.numel() != hq or not sink.is_contiguous()):
+        raise ValueError("sink must be a contiguous float32 tensor of H entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((t_n, hq), dtype=torch.float32, device=q.device)
+    st = psattn_mla_dense_fwd(_ptr(q), _ptr(ckv), _ptr(sink), _ptr(out), _ptr(lse), t_n, hq, d, int(ckv.shape[0]),
+                              int(ckv.stride(0)), float(sm_scale), _dtype_code(q), _stream_handle(q.device))
     check(st)
     return out, lse
 

@@ -329,6 +329,32 @@ def test_mla_validation(lib, kw, status):
     assert ps.psattn_last_error()
 
 
+def _mla_dense(q=FAKE, ckv=FAKE, sink=0, o=FAKE, lse=FAKE, t=16, h=64, d=512, s=100, stride=512, sm=0.04,
+               dt=ps.BF16):
+    return ps.psattn_mla_dense_fwd(q, ckv, sink, o, lse, t, h, d, s, stride, sm, dt, 0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=ps.F32), ps.E_UNSUPPORTED),
+    (dict(d=256), ps.E_UNSUPPORTED),
+    (dict(h=48), ps.E_UNSUPPORTED),
+    (dict(s=15), ps.E_INVAL),          # the cache must hold the 16 query tokens
+    (dict(t=-1), ps.E_INVAL),
+    (dict(stride=500), ps.E_INVAL),
+    (dict(sm=float("nan")), ps.E_INVAL),
+    (dict(ckv=0), ps.E_INVAL),
+    (dict(q=FAKE + 4), ps.E_INVAL),
+    (dict(sink=FAKE + 2), ps.E_INVAL),
+])
+def test_mla_dense_validation(lib, kw, status):
+    assert _mla_dense(**kw) == status
+    assert ps.psattn_last_error()
+
+
+def test_mla_dense_empty_enqueues_nothing(lib):
+    assert _mla_dense(t=0, s=0, q=0, o=0, lse=0, ckv=0) == ps.OK
+
+
 def test_mla_no_tokens_enqueues_nothing(lib):
     assert _mla(q=0, ckv=0, idx=0, o=0, lse=0, t=0) == ps.OK
 
