@@ -257,16 +257,20 @@ def test_verify_workspace_reused_across_calls(gpu_lib):
                 f"reused workspace {list(inst.prefix_lens)[:4]} Lx={inst.draft_len} D={inst.d}")
 
 
-def test_verify_register_pass_graph_replays(gpu_lib):
-    """A captured verify call (register split pass and merge) replays to the
-    eager result: three replays, each after an eager call with other inputs
-    on the same workspace and then once more straight after, equal the eager
-    call on the same inputs bit for bit."""
+@pytest.mark.parametrize("lx,hq,hkv,d,kvdt", [
+    (4, 16, 4, 128, BF16),   # 16 stacked rows: the register split pass
+    (8, 16, 2, 256, FP8),    # 64 stacked rows, fp8: the wide split pass
+])
+def test_verify_graph_replays(gpu_lib, lx, hq, hkv, d, kvdt):
+    """A captured verify call (split pass and merge) replays to the eager
+    result: three replays, each after an eager call with other inputs on the
+    same workspace and then once more straight after, equal the eager call on
+    the same inputs bit for bit."""
     import torch
 
-    inst = make_paged([1500, 2300, 40, 800] * 2, 4, 16, 4, 128, kv_dtype=BF16, seed=68, num_pages=600)
-    other = make_paged([1500, 2300, 40, 800] * 2, 4, 16, 4, 128, kv_dtype=BF16, seed=69, num_pages=600)
-    assert inst.draft_len * inst.hq // inst.hkv == 16  # 16 stacked rows: the register split pass
+    plens = [1500, 2300, 40, 800] * 2
+    inst = make_paged(plens, lx, hq, hkv, d, kv_dtype=kvdt, seed=68, num_pages=600, scales=kvdt == FP8)
+    other = make_paged(plens, lx, hq, hkv, d, kv_dtype=kvdt, seed=69, num_pages=600, scales=kvdt == FP8)
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
     def args_of(x):
@@ -275,16 +279,17 @@ def test_verify_register_pass_graph_replays(gpu_lib):
                 to_dev(x.v_ext, x.kv_dtype), x.draft_len, x.max_prefix_len)
 
     a1, a2 = args_of(inst), args_of(other)
-    kw = dict(sm_scale=inst.sm_scale, kv_dtype=BF16)
-    desc = gpu_lib.paged_desc(inst.batch, 4, 16, inst.num_pages, 1, 1, 1, inst.max_prefix_len, 1, 1)
-    ws = torch.full((gpu_lib.psattn_workspace_size(desc, 16, 4, 128, BF16, BF16),), 0x7F, dtype=torch.uint8,
+    kw = dict(sm_scale=inst.sm_scale, kv_dtype=kvdt, k_scale=inst.k_scale, v_scale=inst.v_scale)
+    desc = gpu_lib.paged_desc(inst.batch, lx, 16, inst.num_pages, 1, 1, 1, inst.max_prefix_len, 1, 1)
+    ws = torch.full((gpu_lib.psattn_workspace_size(desc, hq, hkv, d, BF16, kvdt),), 0x7F, dtype=torch.uint8,
                     device="cuda")
     o_e, l_e = gpu_lib.fwd_paged(*a1, **kw, workspace=ws)
     torch.cuda.synchronize()
     compare(to_f64(o_e), to_f64(l_e), *attn_paged(inst.q, inst.k_pool, inst.v_pool, inst.kv_indptr,
                                                   inst.kv_indices, inst.prefix_lens, inst.k_ext, inst.v_ext,
-                                                  inst.draft_len, inst.sm_scale, q_dtype=BF16, kv_dtype=BF16),
-            "bf16", "register pass, eager")
+                                                  inst.draft_len, inst.sm_scale, k_scale=inst.k_scale,
+                                                  v_scale=inst.v_scale, q_dtype=BF16, kv_dtype=kvdt),
+            kind_of(BF16, kvdt), f"graph replay case Lx={lx} D={d}, eager")
     o_g, l_g = torch.empty_like(o_e), torch.empty_like(l_e)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
