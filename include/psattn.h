@@ -268,13 +268,14 @@ size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hk
  *                  multi-level forward (each segment's expansion copies the
  *                  prefix and its ancestors' tokens, and every copy's gradient
  *                  flows back to the stored row).
- *   d            : 64 or 128.  dtype: PSATTN_BF16.  hq / hkv <= 64.
+ *   d            : 64, 128 or 256.  dtype: PSATTN_BF16.  hq / hkv <= 64.
  *   sm_scale     : the forward's logit scale.
  *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,
  *                  256-byte aligned; its contents on entry do not matter.
  * Enqueues five launches on `stream` (row terms, dQ, dK/dV over the items
  * that max_seg_len predicts, dK/dV over any items past that bound, and the
- * conversion).
+ * conversion; at d = 256 the two dK/dV launches run once per half of the
+ * head dimension).
  * dK and dV sum fp32 partials with atomic adds, so their last bits may
  * differ between calls; dQ is deterministic.  Other configurations return
  * PSATTN_E_UNSUPPORTED with nothing enqueued.

@@ -166,7 +166,8 @@ psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t h
   psattn_status st = check_common(d, hq, hkv, hd, dt, dt, &bp->base);
   if (st != PSATTN_OK) return st;
   if (dt != PSATTN_BF16) return fail(PSATTN_E_UNSUPPORTED, "the backward takes bf16 only");
-  if (hd != 128 && hd != 64) return fail(PSATTN_E_UNSUPPORTED, "the backward takes head dims 64 and 128 (got %d)", hd);
+  if (hd != 64 && hd != 128 && hd != 256)
+    return fail(PSATTN_E_UNSUPPORTED, "the backward takes head dims 64, 128 and 256 (got %d)", hd);
   if (bp->base.g > 64) return fail(PSATTN_E_UNSUPPORTED, "the backward takes GQA groups up to 64 (got %d)", bp->base.g);
   const int64_t t = d->total_tokens;
   bp->dq_blocks = bp->base.flat_blocks;

@@ -48,6 +48,15 @@ __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
+// a pointer every lane holds the same value of, as a scalar
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int D>
 struct BCfg {
   static constexpr int ROWB = 2 * D;       // bytes of a bf16 row
@@ -55,25 +64,28 @@ struct BCfg {
   static constexpr int RPK = 1024 / ROWB;  // rows per 1 KiB copy block
   static constexpr int NSTEP = D / 16;     // k-steps over the head dimension
   static constexpr int NDB = D / 32;       // 32-column blocks of the head dimension
-  static_assert(CPR == 16 || CPR == 8, "head dims 128 and 64");
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "head dims 64, 128 and 256");
   // Rows read both ways.  256-byte rows (D = 128): c ^ (4 (r & 3) + (r >> 2 & 3))
-  // as described above.  128-byte rows (D = 64) put two rows in one 256-byte
-  // bank row, so (row parity, slot) must differ across a pass: slot
+  // as described above; 512-byte rows (D = 256) the same (the slot moves
+  // inside its 256-byte half).  128-byte rows (D = 64) put two rows in one
+  // 256-byte bank row, so (row parity, slot) must differ across a pass: slot
   // c ^ (2 (r >> 1 & 3) + (r >> 3 & 1)) does it for the 16-row pass and for the
-  // 4-row x 4-half-chunk transposed pass (checked exhaustively on the host).
+  // 4-row x 4-half-chunk transposed pass (all checked exhaustively on the host).
   __device__ static constexpr int fb(int r) {
-    return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    return CPR != 8 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
   }
   // rows read by rows only (with 128-byte rows, by the row pair)
-  __device__ static constexpr int fk(int r) { return CPR == 16 ? (r & 15) : ((r >> 1) & 7); }
+  __device__ static constexpr int fk(int r) { return CPR != 8 ? (r & 15) : ((r >> 1) & 7); }
 };
 
 // ------------------------------------------------------------------- dQ pass
 // CHAIN: multi-level sharing (seg_parent set): after the item's own walk
 // (the prefix, then its rollout up to its tile), one pass per ancestor
 // segment walks that segment's keys, all visible (the forward's walk).
+// One wave per SIMD at D = 256 (its Q^T and dO^T fragments and dQ^T
+// accumulators alone take 256 registers), two below.
 template <int D, bool CHAIN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2)))
 void bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int BN = 64;
@@ -362,15 +374,22 @@ void bwd_dq_kernel(BwdArgs a) {
 // false the loop below ends after its first pass and compiles to the
 // straight-line kernel; a loop taken by every workgroup changed the schedule
 // of the tile loop and cost about 9% per call.)
-template <int D, bool WALK>
+//
+// DO: head-dim columns of dK / dV one launch accumulates, from column dofs
+// (D up to 128; at D = 256 two launches of 128 columns each, S and dP formed
+// in both, so that the fragments of the full row and two 128-column
+// accumulators fit one wave's registers).
+template <int D, int DO, bool WALK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void bwd_dkdv_kernel(BwdArgs a, int first_item) {
+void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
   using C = BCfg<D>;
+  constexpr int NDO = DO / 32;  // 32-column blocks of the accumulated columns
+  const int dcol = DO == D ? 0 : dofs;  // first accumulated column (a constant when one launch covers all)
   constexpr int RT = 64;                  // stacked query rows per tile
   constexpr int TILE = RT * C::ROWB;      // Q (or dO) tile bytes
   constexpr int NCOPY = TILE / 1024;      // 1 KiB copies per Q (or dO) tile
   constexpr int CPW = 2 * NCOPY / kWaves; // copies per wave per tile
-  constexpr int NBUF = 4;                                        // tile ring (NBUF - 1 tiles ahead)
+  constexpr int NBUF = D >= 256 ? 2 : 4;  // tile ring (NBUF - 1 tiles ahead; 32 KiB tiles at D = 256)
   __shared__ __attribute__((aligned(1024))) char smem[NBUF][2][TILE];  // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float rowv[NBUF][2][RT];     // [buffer][lse2, delta]
   __shared__ __attribute__((aligned(16))) int tokoff[RT];           // token offset of stacked row s
@@ -462,6 +481,9 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
       const int t0 = bi.r0 + tl * TT;
       const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;  // valid stacked rows
       const char* base = src + ((size_t)t0 * a.hq + (size_t)h_kv * G) * C::ROWB;
+      // (at D = 256 the walking variant's loop hides the base's uniformity
+      // from the compiler, which then cannot give the copies a scalar base)
+      if constexpr (D >= 256) base = uniform_ptr(base);
       if (nv == RT) {
   #pragma unroll
         for (int t = 0; t < CPW; ++t) {
@@ -482,6 +504,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
       }
       if (wave < 2) {
         const float* rb = rsrc + (size_t)t0 * a.hq + (size_t)h_kv * G;
+        if constexpr (D >= 256) rb = uniform_ptr(rb);
         uint32_t ro = roff;
         if (nv < RT) {
           const int sl = lane < nv ? lane : nv - 1;
@@ -491,9 +514,9 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
       }
     };
 
-    f32x16_t dk[C::NDB], dv[C::NDB];
+    f32x16_t dk[NDO], dv[NDO];
   #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < NDO; ++db)
   #pragma unroll
       for (int e = 0; e < 16; ++e) {
         dk[db][e] = 0.f;
@@ -557,12 +580,12 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
   #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
   #pragma unroll
-          for (int dbk = 0; dbk < C::NDB; ++dbk) {
+          for (int dbk = 0; dbk < NDO; ++dbk) {
             s16x4_t ov[2], qv[2];
   #pragma unroll
             for (int t = 0; t < 2; ++t) {
               const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
-              const int chunk = 4 * dbk + 2 * hgrp + (ap >> 1);
+              const int chunk = 4 * (dbk + dcol / 32) + 2 * hgrp + (ap >> 1);
               const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
               ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
               qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
@@ -622,14 +645,14 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
     // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
     // c ^ (kr mod the row's chunks)), then adds it with consecutive lanes on
     // consecutive floats.
-    constexpr int SROW = D * 4;
+    constexpr int SROW = DO * 4;
     constexpr int SMASK = SROW / 16 - 1;
     static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
     char* st = &smem[0][0][0] + wave * (32 * SROW);
   #pragma unroll
     for (int which = 0; which < 2; ++which) {
   #pragma unroll
-      for (int dbk = 0; dbk < C::NDB; ++dbk)
+      for (int dbk = 0; dbk < NDO; ++dbk)
   #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
@@ -640,13 +663,13 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item) {
       __syncthreads();
       float* acc = which == 0 ? a.acc_v : a.acc_k;
   #pragma unroll 4
-      for (int p = lane; p < 32 * D; p += 64) {
-        const int kr = p / D;
-        const int f = p % D;
+      for (int p = lane; p < 32 * DO; p += 64) {
+        const int kr = p / DO;
+        const int f = p % DO;
         const int kk = bi.k0 + 32 * wave + kr;
         if (kk < bi.k1) {
           const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ (kr & SMASK)) + 4 * (f & 3));
-          unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + f, x);
+          unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + dcol + f, x);
         }
       }
       __syncthreads();
@@ -732,14 +755,16 @@ int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipSt
       hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
     if ((err = (int)hipGetLastError())) return err;
   }
-  if (dkdv_blocks > 0) {
+  constexpr int DO = D >= 256 ? 128 : D;  // dK / dV columns per key-major launch
+  for (int dofs = 0; dkdv_blocks > 0 && dofs < D; dofs += DO) {
     // the items the host bound predicts, one per workgroup ...
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, false>), dim3((unsigned)dkdv_blocks), dim3(kThreads), 0, s, a, 0);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DO, false>), dim3((unsigned)dkdv_blocks), dim3(kThreads), 0, s, a, 0,
+                       dofs);
     if ((err = (int)hipGetLastError())) return err;
     // ... and any past it (none when the bound holds: the workgroups then find
     // their first item past the end and return)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, true>), dim3((unsigned)(kBwdWalkPerHead * a.hkv)), dim3(kThreads), 0, s,
-                       a, (int)(dkdv_blocks / a.hkv));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DO, true>), dim3((unsigned)(kBwdWalkPerHead * a.hkv)), dim3(kThreads), 0,
+                       s, a, (int)(dkdv_blocks / a.hkv), dofs);
     if ((err = (int)hipGetLastError())) return err;
   }
   const int64_t n8 = a.total_tokens * a.hkv * D / 8;
@@ -756,6 +781,7 @@ int launch_flat_bwd(const BwdArgs& a, int d, int64_t dq_blocks, int64_t dkdv_blo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (d == 128) return launch_bwd_t<128>(a, dq_blocks, dkdv_blocks, s);
   if (d == 64) return launch_bwd_t<64>(a, dq_blocks, dkdv_blocks, s);
+  if (d == 256) return launch_bwd_t<256>(a, dq_blocks, dkdv_blocks, s);
   return (int)hipErrorInvalidValue;
 }
 

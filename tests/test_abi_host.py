@@ -249,7 +249,6 @@ def _bwd(desc, hq=8, hkv=2, d=128, dt=ps.BF16, sm=0.088, ptr=FAKE, lse=FAKE, ws=
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(d=256), ps.E_UNSUPPORTED),
     (dict(dt=ps.F32), ps.E_UNSUPPORTED),
     (dict(dt=ps.FP8), ps.E_UNSUPPORTED),
     (dict(hq=128, hkv=1), ps.E_UNSUPPORTED),   # G = 128 > 64
@@ -272,13 +271,11 @@ def test_bwd_paged_mode_unsupported(lib):
     assert ps.psattn_bwd_workspace_size(_paged(), 8, 2, 128, ps.BF16) == 0
 
 
-def test_bwd_takes_head_dims_64_and_128(lib):
+def test_bwd_takes_head_dims_64_128_and_256(lib):
     desc = _flat(t=96, p=64, n=2, mx=16)
     up = lambda x: (x + 255) // 256 * 256
-    for d in (64, 128):
+    for d in (64, 128, 256):
         assert ps.psattn_bwd_workspace_size(desc, 8, 2, d, ps.BF16) == 2 * up(96 * 8 * 4) + 2 * up(96 * 2 * d * 4) + up(16 * 5)
-    assert ps.psattn_bwd_workspace_size(desc, 8, 2, 256, ps.BF16) == 0
-    assert "head dims 64 and 128" in ps.psattn_last_error()
 
 
 def test_bwd_workspace_size(lib):

@@ -103,9 +103,10 @@ def test_bwd_small_full(gpu_lib, p, lens, hq, hkv):
     (600, [700, 513], 8, 2),        # rows of a key tile span several 512-token chunks
     (300, [200, 128, 1, 77], 32, 8),  # GRPO head layout, small
 ])
-def test_bwd_head_dim_64(gpu_lib, p, lens, hq, hkv):
-    inst = make_flat(p, lens, hq, hkv, 64, dtype=BF16, seed=p + len(lens) + hq + 64)
-    _check(gpu_lib, inst, label=f"D=64 P={p} lens={lens} hq={hq} hkv={hkv}")
+@pytest.mark.parametrize("d", [64, 256])
+def test_bwd_head_dims_64_and_256(gpu_lib, p, lens, hq, hkv, d):
+    inst = make_flat(p, lens, hq, hkv, d, dtype=BF16, seed=p + len(lens) + hq + d)
+    _check(gpu_lib, inst, label=f"D={d} P={p} lens={lens} hq={hq} hkv={hkv}")
 
 
 def test_bwd_grpo_block(gpu_lib):

@@ -95,9 +95,10 @@ def test_tree_bwd_seeded_forest(gpu_lib, seed):
     _check(gpu_lib, inst, parents, f"forest seed={seed} parents={parents.tolist()}")
 
 
-def test_tree_bwd_head_dim_64(gpu_lib):
-    inst = make_flat(90, [33, 65, 70, 20], 8, 2, 64, dtype=BF16, seed=64)
-    _check(gpu_lib, inst, [-1, 0, 1, 0], "D=64 chain")
+@pytest.mark.parametrize("d", [64, 256])
+def test_tree_bwd_head_dims_64_and_256(gpu_lib, d):
+    inst = make_flat(90, [33, 65, 70, 20], 8, 2, d, dtype=BF16, seed=d)
+    _check(gpu_lib, inst, [-1, 0, 1, 0], f"D={d} chain")
 
 
 def test_tree_bwd_all_roots_is_one_level(gpu_lib):
