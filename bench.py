@@ -513,7 +513,7 @@ def main():
     json_out = sys.stdout
     sys.stdout = sys.stderr
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
 
