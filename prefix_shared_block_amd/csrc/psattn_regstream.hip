@@ -9,11 +9,13 @@
 // bandwidth is the only real bound (16 rows against thousands of keys: 16
 // flop per byte) this file does both, arranged for HBM streaming:
 //
-//  * paged_reg_kernel: one wave per workgroup and one (request, kv head,
-//    split) per wave; the waves are independent (no barriers), so a CU holds
-//    several of them.  The last split of each (request, kv head) also runs
-//    the causal draft block as one extra 16-key stage (draft row j sees draft
-//    keys 0..j), so its partial already contains it;
+//  * paged_reg_kernel: one workgroup per (request, kv head, split), of
+//    reg_waves(D) waves (8 up to D = 128, 4 at D = 256), each streaming its
+//    own contiguous run of the split's stages with no barrier until the
+//    waves' results are merged in LDS at the end.  The last split of each
+//    (request, kv head) also runs the causal draft block as one extra 16-key
+//    stage (draft row j sees draft keys 0..j), so its partial already
+//    contains it;
 //  * paged_merge_kernel: one wave per (stacked row, 64 columns) merges the
 //    splits' partial results by log-sum-exp and applies v_scale.
 //
@@ -34,7 +36,7 @@
 //    v_mfma_f32_16x16x32_bf16 for S^T = K Q^T, V columns with the transpose
 //    read ds_read_b64_tr_b16 as the A operand of v_mfma_f32_16x16x16_bf16 for
 //    O^T += V^T P^T, whose B operand P^T is the score registers themselves.
-//    The tiles are private to the wave, so no barrier is ever needed;
+//    The tiles are private to the wave, so the stage loop needs no barrier;
 //  * k_scale is folded into the logit scale and v_scale is applied by the
 //    combine stage;
 //  * online softmax in the log2 domain with lazy rescaling (the running
