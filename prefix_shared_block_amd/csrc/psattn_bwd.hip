@@ -528,74 +528,100 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
     const int ap = li & 3;
     const int hgrp = l32 >> 4;
 
-    auto math = [&](int bsel, int t0, int nv, auto maskc) __attribute__((always_inline)) {
+    // One 32-row block rb of the tile: S and dP products, softmax terms, then
+    // the dV / dK updates.  The two blocks of a tile are software-pipelined
+    // (block 1's products beside block 0's softmax, block 0's updates beside
+    // block 1's softmax): one wave per SIMD has no second wave to overlap its
+    // matrix and vector work.
+    auto sdp = [&](const char* qt, const char* dt, int rb, f32x16_t& sc, f32x16_t& dp) __attribute__((always_inline)) {
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sc[e] = 0.f;
+        dp[e] = 0.f;
+      }
+      const int row = 32 * rb + l32;
+  #pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
+      }
+  #pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
+      }
+    };
+    // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
+    auto soft = [&](const float* l2, const float* dl, int rb, int t0, int nv, const f32x16_t& sc, const f32x16_t& dp,
+                    bf16x8_t (&pb)[2], bf16x8_t (&db_)[2], auto maskc) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(maskc)::value;
+  #pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int s0 = 32 * rb + 8 * q4 + 4 * g;  // rows s0 .. s0 + 3 of regs 4 q4 .. 4 q4 + 3
+        const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(l2 + s0);
+        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dl + s0);
+        int4 tv;
+        if constexpr (MASK) tv = *reinterpret_cast<const int4*>(tokoff + s0);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          float p = fast_exp2(__builtin_fmaf(sc[i], c, -lv[e]));
+          if constexpr (MASK) {
+            const int te = e == 0 ? tv.x : (e == 1 ? tv.y : (e == 2 ? tv.z : tv.w));
+            const bool vis = (s0 + e < nv) && (key <= t0 + te);
+            p = vis ? p : 0.f;
+          }
+          pb[i >> 3][i & 7] = (__bf16)p;
+          db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dv4[e]));
+        }
+      }
+    };
+    // dV^T += dO^T P and dK^T += Q^T dS: A operand lane (d, g) = rows
+    // 32 rb + 16 ks + 8 t + 4 g + 0..3 of column d, read transposed
+    auto upd = [&](const char* qt, const char* dt, int rb, const bf16x8_t (&pb)[2], const bf16x8_t (&db_)[2])
+        __attribute__((always_inline)) {
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+  #pragma unroll
+        for (int dbk = 0; dbk < NDO; ++dbk) {
+          s16x4_t ov[2], qv[2];
+  #pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
+            const int chunk = 4 * (dbk + dcol / 32) + 2 * hgrp + (ap >> 1);
+            const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
+            ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
+            qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
+          }
+          const s16x8_t o8 = {ov[0][0], ov[0][1], ov[0][2], ov[0][3], ov[1][0], ov[1][1], ov[1][2], ov[1][3]};
+          const s16x8_t q8 = {qv[0][0], qv[0][1], qv[0][2], qv[0][3], qv[1][0], qv[1][1], qv[1][2], qv[1][3]};
+          dv[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, o8), pb[ks], dv[dbk], 0, 0, 0);
+          dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q8), db_[ks], dk[dbk], 0, 0, 0);
+        }
+      }
+    };
+    static_assert(RT == 64, "two 32-row blocks per tile");
+    auto math = [&](int bsel, int t0, int nv, auto maskc) __attribute__((always_inline)) {
       const char* qt = smem[bsel][0];
       const char* dt = smem[bsel][1];
       const float* l2 = rowv[bsel][0];
       const float* dl = rowv[bsel][1];
-  #pragma unroll
-      for (int rb = 0; rb < RT / 32; ++rb) {
-        // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
-        f32x16_t sc, dp;
-  #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sc[e] = 0.f;
-          dp[e] = 0.f;
-        }
-        const int row = 32 * rb + l32;
-  #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s) {
-          const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
-        }
-  #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s) {
-          const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
-        }
-        bf16x8_t pb[2], db_[2];  // k-step ks (16 rows): regs 8 ks .. 8 ks + 7
-  #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int s0 = 32 * rb + 8 * q4 + 4 * g;  // rows s0 .. s0 + 3 of regs 4 q4 .. 4 q4 + 3
-          const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(l2 + s0);
-          const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dl + s0);
-          int4 tv;
-          if constexpr (MASK) tv = *reinterpret_cast<const int4*>(tokoff + s0);
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * q4 + e;
-            float p = fast_exp2(__builtin_fmaf(sc[i], c, -lv[e]));
-            if constexpr (MASK) {
-              const int te = e == 0 ? tv.x : (e == 1 ? tv.y : (e == 2 ? tv.z : tv.w));
-              const bool vis = (s0 + e < nv) && (key <= t0 + te);
-              p = vis ? p : 0.f;
-            }
-            pb[i >> 3][i & 7] = (__bf16)p;
-            db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dv4[e]));
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS: A operand lane (d, g) = rows
-        // 32 rb + 16 ks + 8 t + 4 g + 0..3 of column d, read transposed
-  #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-  #pragma unroll
-          for (int dbk = 0; dbk < NDO; ++dbk) {
-            s16x4_t ov[2], qv[2];
-  #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
-              const int chunk = 4 * (dbk + dcol / 32) + 2 * hgrp + (ap >> 1);
-              const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
-              ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
-              qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
-            }
-            const s16x8_t o8 = {ov[0][0], ov[0][1], ov[0][2], ov[0][3], ov[1][0], ov[1][1], ov[1][2], ov[1][3]};
-            const s16x8_t q8 = {qv[0][0], qv[0][1], qv[0][2], qv[0][3], qv[1][0], qv[1][1], qv[1][2], qv[1][3]};
-            dv[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, o8), pb[ks], dv[dbk], 0, 0, 0);
-            dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q8), db_[ks], dk[dbk], 0, 0, 0);
-          }
-        }
+      f32x16_t sc0, dp0, sc1, dp1;
+      bf16x8_t pb0[2], db0[2], pb1[2], db1[2];
+      if constexpr (D <= 128) {
+        sdp(qt, dt, 0, sc0, dp0);
+        sdp(qt, dt, 1, sc1, dp1);
+        soft(l2, dl, 0, t0, nv, sc0, dp0, pb0, db0, maskc);
+        upd(qt, dt, 0, pb0, db0);
+        soft(l2, dl, 1, t0, nv, sc1, dp1, pb1, db1, maskc);
+        upd(qt, dt, 1, pb1, db1);
+      } else {  // at D = 256 the second block's scores would not fit beside the fragments
+        sdp(qt, dt, 0, sc0, dp0);
+        soft(l2, dl, 0, t0, nv, sc0, dp0, pb0, db0, maskc);
+        upd(qt, dt, 0, pb0, db0);
+        sdp(qt, dt, 1, sc1, dp1);
+        soft(l2, dl, 1, t0, nv, sc1, dp1, pb1, db1, maskc);
+        upd(qt, dt, 1, pb1, db1);
       }
     };
 
