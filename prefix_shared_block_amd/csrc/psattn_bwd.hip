@@ -668,38 +668,66 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
     }
 
     // Add the item's partial dK^T / dV^T into the fp32 accumulators.  Each wave
-    // stages its [32 keys][D] block in LDS (16-byte chunk c of key row kr at
-    // c ^ (kr mod the row's chunks)), then adds it with consecutive lanes on
-    // consecutive floats.
+    // stages its two [32 keys][DO] blocks in LDS (16-byte chunk c of key row kr
+    // at c ^ (kr mod the row's chunks)), then adds them with consecutive lanes
+    // on consecutive floats.  The staging areas are the wave's own (the tile
+    // loop's last barrier has retired every read of the ring), so no barrier
+    // is needed; the adds run a fixed count with no branch, so that their LDS
+    // reads issue in batches: a key row past the item's end adds 0 to the
+    // item's last key (the accumulators start at +0 and never hold -0, so the
+    // add changes nothing).  A per-lane test around each add had serialised
+    // one LDS round trip per add (about 10 us per item).
     constexpr int SROW = DO * 4;
     constexpr int SMASK = SROW / 16 - 1;
-    static_assert(kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
-    char* st = &smem[0][0][0] + wave * (32 * SROW);
+    static_assert(2 * kWaves * 32 * SROW <= NBUF * 2 * TILE, "staging fits in the tiles");
+    char* const st_v = &smem[0][0][0] + wave * (32 * SROW);
+    char* const st_k = st_v + kWaves * (32 * SROW);
   #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+    for (int dbk = 0; dbk < NDO; ++dbk)
   #pragma unroll
-      for (int dbk = 0; dbk < NDO; ++dbk)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
+        const int off = l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ (l32 & SMASK));
+        *reinterpret_cast<f32x4_t*>(st_v + off) =
+            f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]};
+        *reinterpret_cast<f32x4_t*>(st_k + off) =
+            f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
+      }
+    {
+      const int kbase = bi.k0 + 32 * wave;
   #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          // C layout: lane (key l32, g), regs 4 q4 .. 4 q4 + 3 hold d = 32 dbk + 8 q4 + 4 g .. +3
-          const f32x4_t x = which == 0 ? f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]}
-                                       : f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
-          *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ (l32 & SMASK))) = x;
-        }
-      __syncthreads();
-      float* acc = which == 0 ? a.acc_v : a.acc_k;
-  #pragma unroll 4
-      for (int p = lane; p < 32 * DO; p += 64) {
-        const int kr = p / DO;
-        const int f = p % DO;
-        const int kk = bi.k0 + 32 * wave + kr;
-        if (kk < bi.k1) {
-          const float x = *reinterpret_cast<const float*>(st + kr * SROW + 16 * ((f >> 2) ^ (kr & SMASK)) + 4 * (f & 3));
-          unsafeAtomicAdd(acc + ((size_t)kk * a.hkv + h_kv) * D + dcol + f, x);
+      for (int which = 0; which < 2; ++which) {
+        const char* stw = which == 0 ? st_v : st_k;
+        float* acc = which == 0 ? a.acc_v : a.acc_k;
+        // batches of 8: the reads first (the compiler keeps memory operations
+        // in order around an atomic, so they are written ahead of the adds)
+        constexpr int NI = 32 * DO / 64;
+        static_assert(NI % 8 == 0, "batches of 8");
+  #pragma unroll 1
+        for (int i0 = 0; i0 < NI; i0 += 8) {
+          float x[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int p = lane + 64 * (i0 + j);
+            const int kr = p / DO;
+            const int f = p % DO;
+            x[j] = *reinterpret_cast<const float*>(stw + kr * SROW + 16 * ((f >> 2) ^ (kr & SMASK)) + 4 * (f & 3));
+          }
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int p = lane + 64 * (i0 + j);
+            const int kr = p / DO;
+            const int f = p % DO;
+            const int kk = kbase + kr;
+            const bool ok = kk < bi.k1;
+            const int kc = ok ? kk : bi.k1 - 1;
+            unsafeAtomicAdd(acc + ((size_t)kc * a.hkv + h_kv) * D + dcol + f, ok ? x[j] : 0.f);
+          }
         }
       }
-      __syncthreads();
     }
+    // the walking launch's next item refills the ring the staging areas lie in
+    if constexpr (WALK) __syncthreads();
     if constexpr (!WALK) return;
   }  // items
 }
