@@ -398,6 +398,16 @@ void flat2_kernel(FlatArgs a) {
   if (valid && g == 0) a.lse[qrow] = (m_run + fast_log2(lt)) * kLn2;
   __syncthreads();
   constexpr int NOUT = kWaveRows * C::CPR / 64;  // 16-byte stores per lane
+  // every staged chunk is read first (in bounds whatever the row), so that the
+  // reads issue together instead of one round trip behind each row's test
+  u32x4_t x[NOUT];
+#pragma unroll
+  for (int k = 0; k < NOUT; ++k) {
+    const int p = 64 * k + lane;
+    const int row = p / C::CPR;
+    const int ch = p % C::CPR;
+    x[k] = *reinterpret_cast<const u32x4_t*>(ost + row * C::ROWB + 16 * (ch ^ (row & (C::CPR - 1))));
+  }
 #pragma unroll
   for (int k = 0; k < NOUT; ++k) {
     const int p = 64 * k + lane;
@@ -408,9 +418,8 @@ void flat2_kernel(FlatArgs a) {
     const int hh = rr - tk * a.g;
     const int tkn = it.q_begin + tk;
     if (tk < a.tile_tokens && tkn < it.q_end) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ost + row * C::ROWB + 16 * (ch ^ (row & (C::CPR - 1))));
       __bf16* op = reinterpret_cast<__bf16*>(a.o) + ((size_t)tkn * a.hq + h_kv * a.g + hh) * D + 8 * ch;
-      __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(op));
+      __builtin_nontemporal_store(x[k], reinterpret_cast<u32x4_t*>(op));
     }
   }
 }

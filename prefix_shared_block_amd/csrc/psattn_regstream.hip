@@ -354,19 +354,27 @@ void paged_reg_kernel(PagedArgs a) {
       const int r = pc / (D / 4);
       const int c4 = pc - r * (D / 4);
       if (r >= a.rows) continue;
+      // every wave's values are read first and combined with selects: a
+      // branch per wave kept each read one LDS round trip behind the last
+      float mw[W], lw[W];
+      f32x4_t xw[W];
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        mw[w] = base[w * stride_w + 16 * D + r];
+        lw[w] = base[w * stride_w + 16 * D + 16 + r];
+        xw[w] = *reinterpret_cast<const f32x4_t*>(base + w * stride_w + r * D + 4 * c4);
+      }
       float mx = kNegBig;
 #pragma unroll
-      for (int w = 0; w < W; ++w) mx = fmaxf(mx, base[w * stride_w + 16 * D + r]);
+      for (int w = 0; w < W; ++w) mx = fmaxf(mx, mw[w]);
       float lsum = 0.f;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < W; ++w) {
-        const float lw = base[w * stride_w + 16 * D + 16 + r];
-        if (lw > 0.f) {
-          const float sc = fast_exp2(base[w * stride_w + 16 * D + r] - mx);
-          lsum += lw * sc;
-          acc += sc * *reinterpret_cast<const f32x4_t*>(base + w * stride_w + r * D + 4 * c4);
-        }
+        // a wave that saw no key has l = 0 and a zero accumulator
+        const float sc = lw[w] > 0.f ? fast_exp2(mw[w] - mx) : 0.f;
+        lsum += lw[w] * sc;
+        acc += sc * xw[w];
       }
       const bool empty = !(lsum > 0.f);
       const float inv = empty ? 0.f : 1.0f / lsum;

@@ -461,10 +461,15 @@ void paged_wide_kernel(PagedArgs a) {
     const size_t prow = (((size_t)b * a.hkv + h_kv) * a.n_splits + it.split) * a.rows + myrow;
     // the partial O in bf16: half the bytes written here and read by the merge
     __bf16* po = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
+    // the other half's values are all read before the first store (one read
+    // issued per store left each store an LDS round trip behind the last)
+    f32x4_t x1s[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) x1s[db] = *reinterpret_cast<const f32x4_t*>(mo + myrow * D + 16 * db + 4 * g);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       const int d0 = 16 * db + 4 * g;
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(mo + myrow * D + d0);
+      const f32x4_t x1 = x1s[db];
       f32x4_t r;
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[e] = (w0 != 0.f ? w0 * o[db][e] : 0.f) + (w1 != 0.f ? w1 * x1[e] : 0.f);
