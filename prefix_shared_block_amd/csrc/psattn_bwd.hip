@@ -540,15 +540,33 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
         dp[e] = 0.f;
       }
       const int row = 32 * rb + l32;
+      if constexpr (D <= 128) {
+        // the block's Q and dO fragments are all read before its first product
+        // (the VGPRs they take are free with K^T / V^T in AGPRs)
+        bf16x8_t qa[C::NSTEP], da[C::NSTEP];
   #pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) {
-        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
-      }
+        for (int s = 0; s < C::NSTEP; ++s)
+          qa[s] = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
   #pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) {
-        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
+        for (int s = 0; s < C::NSTEP; ++s)
+          da[s] = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], sc, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[s], vf[s], dp, 0, 0, 0);
+        }
+      } else {
+  #pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
+        }
+  #pragma unroll
+        for (int s = 0; s < C::NSTEP; ++s) {
+          const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
+        }
       }
     };
     // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
@@ -649,6 +667,10 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
       if (p < ntile) issue(p, p);
   #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
+    if constexpr (D <= 128) {
+  #pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
+    }
     wait_tile(0, lastp);
     __syncthreads();
     int n = 0;
