@@ -667,6 +667,10 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
       if (p < ntile) issue(p, p);
   #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
+    // The fragments are only MFMA source operands, which the matrix cores read
+    // from the accumulation registers (AGPRs) directly: pinned there (this
+    // empty statement emits nothing), they leave the VGPRs to the Q / dO
+    // fragments read ahead of each block's products.
     if constexpr (D <= 128) {
   #pragma unroll
       for (int s = 0; s < C::NSTEP; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
