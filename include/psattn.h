@@ -250,7 +250,8 @@ psattn_status psattn_fwd_noalloc(const void* q, const void* k, const void* v, vo
  * Bytes of scratch psattn_bwd needs (flat mode only): lse2 and delta, [T, Hq]
  * fp32 each, fp32 dK / dV accumulators, [T, Hkv, D] each, and a table of
  * the key-major pass's work items (16 bytes each, as many as the host's bound
- * on one kv head's items from the descriptor's scalars).  Host only.
+ * on one kv head's items from the descriptor's scalars, plus one entry for
+ * the first item past that bound).  Host only.
  * Returns 0 and sets the last error on invalid or unsupported input.
  */
 size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hkv, int32_t d,

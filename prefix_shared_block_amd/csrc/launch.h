@@ -69,7 +69,7 @@ struct BwdArgs {
   float* delta;  // sum_d dO O
   float* acc_k;
   float* acc_v;
-  int32_t* item_tab;  // [n_tab][4] the dK/dV items of one kv head: k0, k1, r0, r1 (k1 <= k0: none)
+  int32_t* item_tab;  // [n_tab + 1][4] dK/dV items of one kv head: k0, k1, r0, r1 (k1 <= k0: none); entry n_tab: the first item past the table
   int32_t n_tab;
   const int32_t* seg_offsets;
   const int32_t* seg_parent;  // [N] parent segment (-1: the prefix), or null: one level

@@ -182,7 +182,9 @@ psattn_status check_bwd(const psattn_desc* d, int32_t hq, int32_t hkv, int32_t h
   bp->off_acck = bp->off_delta + round_up(rows, kWsAlign);
   bp->off_accv = bp->off_acck + round_up(acc, kWsAlign);
   bp->off_items = bp->off_accv + round_up(acc, kWsAlign);
-  bp->ws_bytes = t == 0 ? 0 : bp->off_items + round_up((size_t)bp->n_tab * 4 * sizeof(int32_t), kWsAlign);
+  // the table's n_tab entries, then one for the first item past them (which
+  // tells the walking launch whether it has any work)
+  bp->ws_bytes = t == 0 ? 0 : bp->off_items + round_up((size_t)(bp->n_tab + 1) * 4 * sizeof(int32_t), kWsAlign);
   return PSATTN_OK;
 }
 

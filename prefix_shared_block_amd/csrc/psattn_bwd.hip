@@ -397,6 +397,13 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
   const int blk = blockIdx.x;
   const int h_kv = blk % a.hkv;
   const int nper = (int)(gridDim.x / (unsigned)a.hkv);
+  if constexpr (WALK) {
+    // the row-terms pass left the first item past the table in entry n_tab:
+    // when it is none (the host's bound held), no walking workgroup has work,
+    // and one load spares each of them the enumeration
+    const int4 e = *reinterpret_cast<const int4*>(a.item_tab + 4 * (size_t)a.n_tab);
+    if (!(e.y > e.x)) return;
+  }
   for (int item = first_item + blk / a.hkv;; item += nper) {
     // the one-item launch reads its item from the table the row-terms pass
     // wrote (one load instead of a scan over the segments, which for a
@@ -761,11 +768,12 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
 // ------------------------------------------------------- pre and post passes
 // delta and lse2 for rows [T * Hq]: 16 lanes per row (8 elements each); the
 // accumulators are zeroed and the dK/dV item table is written (thread j:
-// item j of a kv head) by the same grid
+// item j of a kv head, j = 0 .. n_tab, the last entry being the first item
+// past the one-item launch) by the same grid
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int64_t nrows, int64_t nacc4) {
   const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gtid < a.n_tab) {
+  if (gtid <= a.n_tab) {
     const BwdItem bi = dkdv_item((int32_t)gtid, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
     const int4 e = bi.valid ? int4{bi.k0, bi.k1, bi.r0, bi.r1} : int4{0, 0, 0, 0};
     *reinterpret_cast<int4*>(a.item_tab + 4 * gtid) = e;
@@ -822,7 +830,7 @@ template <int D>
 int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipStream_t s) {
   const int64_t nrows = a.total_tokens * a.hq;
   const int64_t nacc4 = a.total_tokens * a.hkv * D / 4;
-  const int64_t pre_threads = nrows * (D / 8) > a.n_tab ? nrows * (D / 8) : a.n_tab;
+  const int64_t pre_threads = nrows * (D / 8) > a.n_tab + 1 ? nrows * (D / 8) : a.n_tab + 1;
   int64_t pre_blocks = (pre_threads + 255) / 256;
   if (pre_blocks < 1) pre_blocks = 1;
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, s, a, nrows, nacc4);

@@ -275,18 +275,19 @@ def test_bwd_takes_head_dims_64_128_and_256(lib):
     desc = _flat(t=96, p=64, n=2, mx=16)
     up = lambda x: (x + 255) // 256 * 256
     for d in (64, 128, 256):
-        assert ps.psattn_bwd_workspace_size(desc, 8, 2, d, ps.BF16) == 2 * up(96 * 8 * 4) + 2 * up(96 * 2 * d * 4) + up(16 * 5)
+        assert ps.psattn_bwd_workspace_size(desc, 8, 2, d, ps.BF16) == 2 * up(96 * 8 * 4) + 2 * up(96 * 2 * d * 4) + up(16 * (5 + 1))
 
 
 def test_bwd_workspace_size(lib):
     # lse2 and delta [T, Hq] fp32, then the dK / dV accumulators [T, Hkv, D] fp32, then the table of
-    # one kv head's dK/dV items (16 bytes each), each 256-byte aligned.  Items: P = 64, two
+    # one kv head's dK/dV items (16 bytes each, plus one entry for the first item past them), each
+    # 256-byte aligned.  Items: P = 64, two
     # rollouts of 32 tokens, max_seg_len 16: one prefix key tile with one prefix chunk and
     # 32 / 512 + 2 rollout chunks (bound), and 32 / 128 + 2 rollout key tiles with one chunk each
     t, hq, hkv, d = 96, 8, 2, 128
     up = lambda x: (x + 255) // 256 * 256
     n_items = 1 * (1 + (0 + 2)) + (0 + 2) * 1
-    want = 2 * up(t * hq * 4) + 2 * up(t * hkv * d * 4) + up(16 * n_items)
+    want = 2 * up(t * hq * 4) + 2 * up(t * hkv * d * 4) + up(16 * (n_items + 1))
     assert ps.psattn_bwd_workspace_size(_flat(t=t, p=64, n=2, mx=16), hq, hkv, d, ps.BF16) == want
     assert ps.psattn_bwd_workspace_size(ps.flat_desc(0, 0, 0, 0, 0), hq, hkv, d, ps.BF16) == 0
 
