@@ -13,14 +13,17 @@
 //    rows, the same 64-key tiles and tile order as the forward):
 //      S^T = K Q^T,  P^T = exp2(S^T c - lse2),  dP^T = V dO^T,
 //      dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T  (dQ = sm_scale dQ^T^T);
-//  * bwd_dkdv: a tile of 128 keys of one kv head per workgroup (32 per wave,
-//    their K^T and V^T fragments in registers) against one chunk of the query
-//    rows that see them, streamed as tiles of 64 stacked rows (copied
-//    global -> LDS three tiles ahead in a ring of four buffers):
+//  * bwd_dkdv2 (D up to 128) / bwd_dkdv (D = 256): a tile of 128 keys of one
+//    kv head per workgroup against one chunk of the query rows that see them,
+//    streamed as tiles of 64 stacked rows (copied global -> LDS, one tile
+//    ahead):
 //      S = Q K^T,  P = exp2(S c - lse2),  dP = dO V^T,  dS = P (dP - delta),
 //      dV^T += dO^T P,  dK^T += Q^T dS;
-//    each item adds its partial dK / dV into the fp32 accumulators (a prefix
-//    key is seen by many chunks);
+//    bwd_dkdv2 keeps the keys' K and V rows in LDS, eight waves (two per
+//    SIMD) in pairs over 32 keys, each wave one 32-row block of every tile;
+//    bwd_dkdv keeps a wave's 32 keys' fragments in registers, one wave per
+//    SIMD, in two 128-column passes.  Each item adds its partial dK / dV into
+//    the fp32 accumulators (a prefix key is seen by many chunks);
 //  * bwd_post: dK = sm_scale acc_k and dV = acc_v, to bf16.
 //
 // Tiles that are read both by rows (an MFMA A operand) and transposed
@@ -360,10 +363,10 @@ void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-// --------------------------------------------------------------- dK/dV pass
-// One wave per SIMD: the fixed K^T / V^T fragments (64 VGPRs) and the two
-// accumulators (128) leave too little of a 256-register budget; at two waves
-// per SIMD the spills cost more than the second wave gains.
+// ------------------------------------------------------ dK/dV pass, D = 256
+// (D up to 128 runs the two-wave kernel further below.)  One wave per SIMD,
+// each holding its 32 keys' full K^T / V^T fragments in registers: at
+// D = 256 the key rows would not fit in LDS beside the query tiles.
 //
 // The workgroup takes item first_item + blockIdx / Hkv of its kv head.
 // WALK = true: it then walks on with a stride of the grid's workgroups per kv
@@ -376,9 +379,9 @@ void bwd_dq_kernel(BwdArgs a) {
 // of the tile loop and cost about 9% per call.)
 //
 // DO: head-dim columns of dK / dV one launch accumulates, from column dofs
-// (D up to 128; at D = 256 two launches of 128 columns each, S and dP formed
-// in both, so that the fragments of the full row and two 128-column
-// accumulators fit one wave's registers).
+// (two launches of 128 columns each, S and dP formed in both, so that the
+// fragments of the full row and two 128-column accumulators fit one wave's
+// registers).
 template <int D, int DO, bool WALK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
@@ -536,10 +539,7 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
     const int hgrp = l32 >> 4;
 
     // One 32-row block rb of the tile: S and dP products, softmax terms, then
-    // the dV / dK updates.  The two blocks of a tile are software-pipelined
-    // (block 1's products beside block 0's softmax, block 0's updates beside
-    // block 1's softmax): one wave per SIMD has no second wave to overlap its
-    // matrix and vector work.
+    // the dV / dK updates.
     auto sdp = [&](const char* qt, const char* dt, int rb, f32x16_t& sc, f32x16_t& dp) __attribute__((always_inline)) {
   #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -547,33 +547,15 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
         dp[e] = 0.f;
       }
       const int row = 32 * rb + l32;
-      if constexpr (D <= 128) {
-        // the block's Q and dO fragments are all read before its first product
-        // (the VGPRs they take are free with K^T / V^T in AGPRs)
-        bf16x8_t qa[C::NSTEP], da[C::NSTEP];
   #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s)
-          qa[s] = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
+      }
   #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s)
-          da[s] = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-        __builtin_amdgcn_sched_barrier(0);
-  #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s) {
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[s], sc, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[s], vf[s], dp, 0, 0, 0);
-        }
-      } else {
-  #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s) {
-          const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[s], sc, 0, 0, 0);
-        }
-  #pragma unroll
-        for (int s = 0; s < C::NSTEP; ++s) {
-          const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
-        }
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * ((2 * s + g) ^ C::fb(row)));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[s], dp, 0, 0, 0);
       }
     };
     // lane (key l32, g), reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4
@@ -633,21 +615,14 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
       const float* dl = rowv[bsel][1];
       f32x16_t sc0, dp0, sc1, dp1;
       bf16x8_t pb0[2], db0[2], pb1[2], db1[2];
-      if constexpr (D <= 128) {
-        sdp(qt, dt, 0, sc0, dp0);
-        sdp(qt, dt, 1, sc1, dp1);
-        soft(l2, dl, 0, t0, nv, sc0, dp0, pb0, db0, maskc);
-        upd(qt, dt, 0, pb0, db0);
-        soft(l2, dl, 1, t0, nv, sc1, dp1, pb1, db1, maskc);
-        upd(qt, dt, 1, pb1, db1);
-      } else {  // at D = 256 the second block's scores would not fit beside the fragments
-        sdp(qt, dt, 0, sc0, dp0);
-        soft(l2, dl, 0, t0, nv, sc0, dp0, pb0, db0, maskc);
-        upd(qt, dt, 0, pb0, db0);
-        sdp(qt, dt, 1, sc1, dp1);
-        soft(l2, dl, 1, t0, nv, sc1, dp1, pb1, db1, maskc);
-        upd(qt, dt, 1, pb1, db1);
-      }
+      // one block after the other: at D = 256 a second block's scores would not
+      // fit beside the key fragments
+      sdp(qt, dt, 0, sc0, dp0);
+      soft(l2, dl, 0, t0, nv, sc0, dp0, pb0, db0, maskc);
+      upd(qt, dt, 0, pb0, db0);
+      sdp(qt, dt, 1, sc1, dp1);
+      soft(l2, dl, 1, t0, nv, sc1, dp1, pb1, db1, maskc);
+      upd(qt, dt, 1, pb1, db1);
     };
 
     auto compute = [&](int n, int bsel, auto maskc) __attribute__((always_inline)) {
@@ -674,14 +649,6 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
       if (p < ntile) issue(p, p);
   #pragma unroll
     for (int s = 0; s < C::NSTEP; ++s) asm volatile("" ::"v"(kf[s]), "v"(vf[s]));
-    // The fragments are only MFMA source operands, which the matrix cores read
-    // from the accumulation registers (AGPRs) directly: pinned there (this
-    // empty statement emits nothing), they leave the VGPRs to the Q / dO
-    // fragments read ahead of each block's products.
-    if constexpr (D <= 128) {
-  #pragma unroll
-      for (int s = 0; s < C::NSTEP; ++s) asm volatile("" : "+a"(kf[s]), "+a"(vf[s]));
-    }
     wait_tile(0, lastp);
     __syncthreads();
     int n = 0;
@@ -765,6 +732,321 @@ void bwd_dkdv_kernel(BwdArgs a, int first_item, int dofs) {
   }  // items
 }
 
+// ------------------------------------------------- dK/dV pass, two waves per SIMD
+constexpr int kWaves2 = 8;
+constexpr int kThreads2 = 64 * kWaves2;
+
+// For D up to 128.  Eight waves share the item's 128 keys in pairs: waves w
+// and w + 4 take keys 32 (w % 4) .. +31, and each takes one 32-row block of
+// every 64-row tile (w / 4).  The keys' K and V rows sit in LDS for the whole
+// item (read as the B operands of the S and dP products, in the same swizzle
+// as the Q / dO rows), so that a wave's registers hold only its accumulators
+// and the tile's terms: two waves fit each SIMD, and one wave's softmax and
+// LDS waits overlap the other's matrix work.  The Q / dO tiles are
+// double-buffered (the key rows take the LDS a deeper ring would use).  At
+// the end the pair's two partial sums are added in LDS and then into the fp32
+// accumulators.
+template <int D, bool WALK>
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv2_kernel(BwdArgs a, int first_item) {
+  using C = BCfg<D>;
+  static_assert(D <= 128, "two waves per SIMD up to D = 128");
+  constexpr int NDO = D / 32;
+  constexpr int RT = 64;                   // stacked query rows per tile
+  constexpr int TILE = RT * C::ROWB;       // Q (or dO) tile bytes
+  constexpr int NCOPY = TILE / 1024;       // 1 KiB copies per Q (or dO) tile
+  constexpr int CPW = 2 * NCOPY / kWaves2; // tile copies per wave
+  constexpr int KVB = 128 * C::ROWB;       // the item's K (or V) rows
+  constexpr int KCPW = 2 * (KVB / 1024) / kWaves2;  // key-row copies per wave
+  // one array: [K, V][key row], then [buffer][Q, dO] tiles; at the end the
+  // eight waves' staged partial sums span both
+  __shared__ __attribute__((aligned(1024))) char lds_all[2 * KVB + 2 * 2 * TILE];
+  char (*const kvs)[KVB] = reinterpret_cast<char (*)[KVB]>(lds_all);
+  char (*const smem)[2][TILE] = reinterpret_cast<char (*)[2][TILE]>(lds_all + 2 * KVB);
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][RT];      // [buffer][lse2, delta]
+  __shared__ __attribute__((aligned(16))) int tokoff[RT];            // token offset of stacked row s
+
+  const int blk = blockIdx.x;
+  const int h_kv = blk % a.hkv;
+  const int nper = (int)(gridDim.x / (unsigned)a.hkv);
+  if constexpr (WALK) {
+    const int4 e = *reinterpret_cast<const int4*>(a.item_tab + 4 * (size_t)a.n_tab);
+    if (!(e.y > e.x)) return;
+  }
+  for (int item = first_item + blk / a.hkv;; item += nper) {
+    BwdItem bi;
+    if constexpr (!WALK) {
+      const int4 e = *reinterpret_cast<const int4*>(a.item_tab + 4 * (size_t)item);
+      bi = BwdItem{e.y > e.x ? 1 : 0, e.x, e.y, e.z, e.w};
+    } else {
+      bi = dkdv_item(item, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
+    }
+    if (!bi.valid) return;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    const int kw = wave & 3;   // the pair's 32 keys
+    const int rb = wave >> 2;  // the wave's 32-row block of each tile
+    const int G = a.g;
+    const int TT = RT / G;
+    const int vrows_full = TT * G;
+
+    if (tid < RT) tokoff[tid] = tid / G;
+
+    const int krow = 32 * kw + l32;  // this lane's key row in kvs
+    const int key = bi.k0 + krow;
+
+    // the item's key rows (rows past its end repeat its last key: finite, and
+    // their columns of S never reach a result)
+    {
+      const uint32_t krs = (uint32_t)a.hkv * C::ROWB;
+  #pragma unroll
+      for (int t = 0; t < KCPW; ++t) {
+        const int jb = wave * KCPW + t;                 // 1 KiB block of K (first half) or V
+        const int which = jb / (KVB / 1024);
+        const int jl = jb % (KVB / 1024);
+        const int s = jl * C::RPK + lane / C::CPR;      // key row
+        const int pos = lane % C::CPR;
+        const int kr = bi.k0 + s < bi.k1 ? s : bi.k1 - 1 - bi.k0;  // row offset from the item's first key
+        const char* base = reinterpret_cast<const char*>(which == 0 ? a.k : a.v) +
+                           ((size_t)bi.k0 * a.hkv + h_kv) * C::ROWB;
+        dma16_s(uniform_ptr(base), (uint32_t)kr * krs + 16u * (uint32_t)(pos ^ C::fb(s)),
+                lds_addr(&kvs[which][jl * 1024]));
+      }
+    }
+
+    const int ntile = cdiv32(bi.r1 - bi.r0, TT);
+    const int kmax = bi.k1 - 1;
+    int ndiag = kmax > bi.r0 ? cdiv32(kmax - bi.r0, TT) : 0;
+    ndiag = ndiag < ntile ? ndiag : ntile;
+    const bool all_mask = vrows_full < RT;
+    const bool extra = !all_mask && ((bi.r1 - bi.r0) % TT != 0) && ntile > ndiag;
+    const int nmask = all_mask ? ntile : ndiag + (extra ? 1 : 0);
+    auto tile_of = [&](int n) __attribute__((always_inline)) {
+      if (all_mask || n < ndiag) return n;
+      if (extra) return n == ndiag ? ntile - 1 : n - 1;
+      return n;
+    };
+
+    // tile copies: waves 0..3 the Q tile, 4..7 the dO tile
+    const bool w_isd = wave * CPW >= NCOPY;
+    const char* src = reinterpret_cast<const char*>(w_isd ? a.dout : a.q);
+    const uint32_t tok_stride = (uint32_t)a.hq * C::ROWB;
+    uint32_t coff[CPW];
+  #pragma unroll
+    for (int t = 0; t < CPW; ++t) {
+      const int jb = (wave * CPW + t) % NCOPY;
+      const int s = jb * C::RPK + lane / C::CPR;
+      const int pos = lane % C::CPR;
+      const int sc_ = s < vrows_full ? s : vrows_full - 1;
+      coff[t] = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB + 16u * (uint32_t)(pos ^ C::fb(s));
+    }
+    const float* rsrc = wave == 0 ? a.lse2 : a.delta;
+    const int s_l = lane < vrows_full ? lane : vrows_full - 1;
+    const uint32_t roff = (uint32_t)((s_l / G) * a.hq + (s_l % G)) * 4u;
+
+    auto issue = [&](int n, int bsel) __attribute__((always_inline)) {
+      const int tl = tile_of(n);
+      const int t0 = bi.r0 + tl * TT;
+      const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;
+      const char* base = uniform_ptr(src + ((size_t)t0 * a.hq + (size_t)h_kv * G) * C::ROWB);
+      if (nv == RT) {
+  #pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+          const int jb = (wave * CPW + t) % NCOPY;
+          dma16_s(base, coff[t], lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
+        }
+      } else {
+  #pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+          const int jb = (wave * CPW + t) % NCOPY;
+          const int s = jb * C::RPK + lane / C::CPR;
+          const int pos = lane % C::CPR;
+          const int sc_ = s < nv ? s : nv - 1;
+          const uint32_t off = (uint32_t)(sc_ / G) * tok_stride + (uint32_t)(sc_ % G) * C::ROWB +
+                               16u * (uint32_t)(pos ^ C::fb(s));
+          dma16_s(base, off, lds_addr(&smem[bsel][w_isd ? 1 : 0][jb * 1024]));
+        }
+      }
+      if (wave < 2) {
+        const float* rbp = uniform_ptr(rsrc + (size_t)t0 * a.hq + (size_t)h_kv * G);
+        uint32_t ro = roff;
+        if (nv < RT) {
+          const int sl = lane < nv ? lane : nv - 1;
+          ro = (uint32_t)((sl / G) * a.hq + (sl % G)) * 4u;
+        }
+        dma4_s(rbp, ro, lds_addr(&rowv[bsel][wave][0]));
+      }
+    };
+
+    f32x16_t dk[NDO], dv[NDO];
+  #pragma unroll
+    for (int db = 0; db < NDO; ++db)
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dk[db][e] = 0.f;
+        dv[db][e] = 0.f;
+      }
+    const float c = a.scale_log2;
+    const int li = lane & 15;
+    const int sp = li >> 2;
+    const int ap = li & 3;
+    const int hgrp = l32 >> 4;
+    const char* kt = kvs[0];
+    const char* vt = kvs[1];
+
+    // the wave's block of one tile: S = Q K^T and dP = dO V^T (lane: key l32,
+    // reg i: stacked row 32 rb + 8 (i / 4) + 4 g + i % 4), the softmax terms,
+    // then dV^T += dO^T P and dK^T += Q^T dS over the block's 32 rows
+    auto math = [&](int bsel, int t0, int nv, auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
+      const char* qt = smem[bsel][0];
+      const char* dt = smem[bsel][1];
+      const float* l2 = rowv[bsel][0];
+      const float* dl = rowv[bsel][1];
+      f32x16_t sc, dp;
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sc[e] = 0.f;
+        dp[e] = 0.f;
+      }
+      const int row = 32 * rb + l32;
+  #pragma unroll
+      for (int s = 0; s < C::NSTEP; ++s) {
+        const int ch = (2 * s + g);
+        const bf16x8_t qa = *reinterpret_cast<const bf16x8_t*>(qt + row * C::ROWB + 16 * (ch ^ C::fb(row)));
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kt + krow * C::ROWB + 16 * (ch ^ C::fb(krow)));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf, sc, 0, 0, 0);
+        const bf16x8_t da = *reinterpret_cast<const bf16x8_t*>(dt + row * C::ROWB + 16 * (ch ^ C::fb(row)));
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt + krow * C::ROWB + 16 * (ch ^ C::fb(krow)));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf, dp, 0, 0, 0);
+      }
+      bf16x8_t pb[2], db_[2];
+  #pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int s0 = 32 * rb + 8 * q4 + 4 * g;
+        const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(l2 + s0);
+        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(dl + s0);
+        int4 tv;
+        if constexpr (MASK) tv = *reinterpret_cast<const int4*>(tokoff + s0);
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * q4 + e;
+          float p = fast_exp2(__builtin_fmaf(sc[i], c, -lv[e]));
+          if constexpr (MASK) {
+            const int te = e == 0 ? tv.x : (e == 1 ? tv.y : (e == 2 ? tv.z : tv.w));
+            const bool vis = (s0 + e < nv) && (key <= t0 + te);
+            p = vis ? p : 0.f;
+          }
+          pb[i >> 3][i & 7] = (__bf16)p;
+          db_[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dv4[e]));
+        }
+      }
+  #pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+  #pragma unroll
+        for (int dbk = 0; dbk < NDO; ++dbk) {
+          s16x4_t ov[2], qv[2];
+  #pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int rr = 32 * rb + 16 * ks + 8 * t + 4 * g + sp;
+            const int chunk = 4 * dbk + 2 * hgrp + (ap >> 1);
+            const int off = rr * C::ROWB + 16 * (chunk ^ C::fb(rr)) + 8 * (ap & 1);
+            ov[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, dt + off));
+            qv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(PB_LDS_PTR(s16x4_t, qt + off));
+          }
+          const s16x8_t o8 = {ov[0][0], ov[0][1], ov[0][2], ov[0][3], ov[1][0], ov[1][1], ov[1][2], ov[1][3]};
+          const s16x8_t q8 = {qv[0][0], qv[0][1], qv[0][2], qv[0][3], qv[1][0], qv[1][1], qv[1][2], qv[1][3]};
+          dv[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, o8), pb[ks], dv[dbk], 0, 0, 0);
+          dk[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, q8), db_[ks], dk[dbk], 0, 0, 0);
+        }
+      }
+    };
+    auto compute = [&](int n, int bsel, auto maskc) __attribute__((always_inline)) {
+      const int tl = tile_of(n);
+      const int t0 = bi.r0 + tl * TT;
+      const int nv = (bi.r1 - t0 < TT ? bi.r1 - t0 : TT) * G;
+      math(bsel, t0, nv, maskc);
+    };
+
+    // the key rows and the first tile, then one tile ahead: a tile's copies
+    // are the only vector-memory operations in flight when it is awaited
+    if (ntile > 0) issue(0, 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+    int n = 0;
+    for (; n < nmask; ++n) {
+      if (n + 1 < ntile) issue(n + 1, (n + 1) & 1);
+      compute(n, n & 1, std::true_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    for (; n < ntile; ++n) {
+      if (n + 1 < ntile) issue(n + 1, (n + 1) & 1);
+      compute(n, n & 1, std::false_type{});
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+
+    // The pair's partial sums, dV then dK: every wave stages its [32 keys][D]
+    // block (16-byte chunk c of key row kr at c ^ (kr mod the row's chunks);
+    // the loop's last barrier has retired every read of the LDS), then wave w
+    // of the pair adds keys 16 (w / 4) .. +15 of both blocks into the fp32
+    // accumulators, with consecutive lanes on consecutive floats, in a fixed
+    // count of adds (a key past the item adds 0 to its last key).
+    constexpr int SROW = D * 4;
+    constexpr int SMASK = SROW / 16 - 1;
+    static_assert(kWaves2 * 32 * SROW <= 2 * KVB + 4 * TILE, "staging fits");
+    char* const stg = lds_all;  // wave w's block at w * 32 SROW
+  #pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      char* st = stg + wave * (32 * SROW);
+  #pragma unroll
+      for (int dbk = 0; dbk < NDO; ++dbk)
+  #pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4_t x = which == 0 ? f32x4_t{dv[dbk][4 * q4], dv[dbk][4 * q4 + 1], dv[dbk][4 * q4 + 2], dv[dbk][4 * q4 + 3]}
+                                       : f32x4_t{dk[dbk][4 * q4], dk[dbk][4 * q4 + 1], dk[dbk][4 * q4 + 2], dk[dbk][4 * q4 + 3]};
+          *reinterpret_cast<f32x4_t*>(st + l32 * SROW + 16 * ((8 * dbk + 2 * q4 + g) ^ (l32 & SMASK))) = x;
+        }
+      __syncthreads();
+      const char* sa = stg + kw * (32 * SROW);        // rows 32 rb' + ..: the pair's rb = 0 wave
+      const char* sb = stg + (kw + 4) * (32 * SROW);  // and its rb = 1 partner
+      float* acc = which == 0 ? a.acc_v : a.acc_k;
+      const int kbase = bi.k0 + 32 * kw + 16 * rb;
+      constexpr int NI = 16 * D / 64;
+      static_assert(NI % 8 == 0, "batches of 8");
+  #pragma unroll 1
+      for (int i0 = 0; i0 < NI; i0 += 8) {
+        float x[8];
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = lane + 64 * (i0 + j);
+          const int kr = 16 * rb + p / D;
+          const int f = p % D;
+          const int o = kr * SROW + 16 * ((f >> 2) ^ (kr & SMASK)) + 4 * (f & 3);
+          x[j] = *reinterpret_cast<const float*>(sa + o) + *reinterpret_cast<const float*>(sb + o);
+        }
+  #pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = lane + 64 * (i0 + j);
+          const int kk = kbase + p / D;
+          const int f = p % D;
+          const bool ok = kk < bi.k1;
+          const int kc = ok ? kk : bi.k1 - 1;
+          unsafeAtomicAdd(acc + ((size_t)kc * a.hkv + h_kv) * D + f, ok ? x[j] : 0.f);
+        }
+      }
+      // the next staging (and a walking launch's next item) overwrite these areas
+      __syncthreads();
+    }
+    if constexpr (!WALK) return;
+  }  // items
+}
+
 // ------------------------------------------------------- pre and post passes
 // delta and lse2 for rows [T * Hq]: 16 lanes per row (8 elements each); the
 // accumulators are zeroed and the dK/dV item table is written (thread j:
@@ -843,7 +1125,19 @@ int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipSt
       hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
     if ((err = (int)hipGetLastError())) return err;
   }
-  constexpr int DO = D >= 256 ? 128 : D;  // dK / dV columns per key-major launch
+  if constexpr (D <= 128) {
+    if (dkdv_blocks > 0) {
+      // the items the host bound predicts, one per workgroup, then any past it
+      // (none when the bound holds: the walking workgroups then return at once)
+      hipLaunchKernelGGL((bwd_dkdv2_kernel<D, false>), dim3((unsigned)dkdv_blocks), dim3(kThreads2), 0, s, a, 0);
+      if ((err = (int)hipGetLastError())) return err;
+      hipLaunchKernelGGL((bwd_dkdv2_kernel<D, true>), dim3((unsigned)(kBwdWalkPerHead * a.hkv)), dim3(kThreads2), 0,
+                         s, a, (int)(dkdv_blocks / a.hkv));
+      if ((err = (int)hipGetLastError())) return err;
+    }
+  }
+  if constexpr (D >= 256) {
+  constexpr int DO = 128;  // dK / dV columns per key-major launch
   for (int dofs = 0; dkdv_blocks > 0 && dofs < D; dofs += DO) {
     // the items the host bound predicts, one per workgroup ...
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, DO, false>), dim3((unsigned)dkdv_blocks), dim3(kThreads), 0, s, a, 0,
@@ -854,6 +1148,7 @@ int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipSt
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, DO, true>), dim3((unsigned)(kBwdWalkPerHead * a.hkv)), dim3(kThreads), 0,
                        s, a, (int)(dkdv_blocks / a.hkv), dofs);
     if ((err = (int)hipGetLastError())) return err;
+  }
   }
   const int64_t n8 = a.total_tokens * a.hkv * D / 8;
   if (n8 > 0) {
