@@ -273,8 +273,9 @@ size_t psattn_bwd_workspace_size(const psattn_desc* desc, int32_t hq, int32_t hk
  *   sm_scale     : the forward's logit scale.
  *   workspace    : device scratch of psattn_bwd_workspace_size() bytes,
  *                  256-byte aligned; its contents on entry do not matter.
- * Enqueues five launches on `stream` (row terms, dQ, dK/dV over the items
- * that max_seg_len predicts, dK/dV over any items past that bound, and the
+ * Enqueues four launches on `stream` (dQ, which also forms the row terms,
+ * zeroes the accumulators and writes the item table; dK/dV over the items
+ * that max_seg_len predicts; dK/dV over any items past that bound; and the
  * conversion; at d = 256 the two dK/dV launches run once per half of the
  * head dimension).
  * dK and dV sum fp32 partials with atomic adds, so their last bits may

@@ -7,10 +7,10 @@
 // visibility (prefix keys seen by every later row, a rollout's keys only by
 // its own later rows), computed here without any expansion:
 //
-//  * bwd_pre: delta = sum_d dO O and lse2 = LSE log2(e) per (row, query
-//    head); zeroes the fp32 dK / dV accumulators;
 //  * bwd_dq: one forward work item per workgroup (4 waves x 32 stacked query
-//    rows, the same 64-key tiles and tile order as the forward):
+//    rows, the same 64-key tiles and tile order as the forward); it also
+//    forms its rows' delta = sum_d dO O and lse2 = LSE log2(e), zeroes the
+//    fp32 dK / dV accumulators and writes the dK/dV item table:
 //      S^T = K Q^T,  P^T = exp2(S^T c - lse2),  dP^T = V dO^T,
 //      dS^T = P^T (dP^T - delta),  dQ^T += K^T dS^T  (dQ = sm_scale dQ^T^T);
 //  * bwd_dkdv2 (D up to 128) / bwd_dkdv (D = 256): a tile of 128 keys of one
@@ -98,6 +98,33 @@ void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][K, V]
 
   const int blk = blockIdx.x;
+  // The launch's other duties, whatever the workgroup's item: zero the fp32
+  // dK / dV accumulators and write the key-major pass's item table (entry j:
+  // item j of a kv head; entry n_tab: the first item past the one-item
+  // launch), both read only by the later dK/dV launches.
+  // (workgroup-uniform loop bounds, so that control flow reconverges at
+  // every step and the copies' base addresses stay scalar below)
+  {
+    const int64_t nthr = (int64_t)gridDim.x * kThreads;
+    const int64_t g0 = (int64_t)blk * kThreads;
+    const int64_t nacc4 = (int64_t)a.total_tokens * a.hkv * (D / 4);
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i0 = g0; i0 < nacc4; i0 += nthr) {
+      const int64_t i = i0 + threadIdx.x;
+      if (i < nacc4) {
+        reinterpret_cast<f32x4_t*>(a.acc_k)[i] = z;
+        reinterpret_cast<f32x4_t*>(a.acc_v)[i] = z;
+      }
+    }
+    for (int64_t j0 = g0; j0 <= a.n_tab; j0 += nthr) {
+      const int64_t j = j0 + threadIdx.x;
+      if (j <= a.n_tab) {
+        const BwdItem bi = dkdv_item((int32_t)j, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
+        const int4 e = bi.valid ? int4{bi.k0, bi.k1, bi.r0, bi.r1} : int4{0, 0, 0, 0};
+        *reinterpret_cast<int4*>(a.item_tab + 4 * j) = e;
+      }
+    }
+  }
   const int h_kv = blk % a.hkv;
   const Item it = flat_item(blk / a.hkv, h_kv, a.prefix_len, a.nseg, a.seg_offsets, a.tile_tokens);
   if (it.kind == kNone) return;
@@ -126,9 +153,27 @@ void bwd_dq_kernel(BwdArgs a) {
       df[s] = *reinterpret_cast<const bf16x8_t*>(dp + 16 * s + 8 * g);
     }
   }
-  // rows outside the item weigh nothing: lse2 = +inf makes their P zero
-  const float lse2 = valid ? a.lse2[qrow] : __builtin_inff();
-  const float delta = valid ? a.delta[qrow] : 0.f;
+  // The row terms, formed here for the item's rows (every query row belongs
+  // to exactly one dQ item) and written for the key-major pass:
+  // delta = sum_d dO O (this lane's dims, then the row's other lane group)
+  // and lse2 = LSE log2 e.  Rows outside the item weigh nothing: lse2 = +inf
+  // makes their P zero.
+  float delta = 0.f;
+  if (valid) {
+    const __bf16* op = reinterpret_cast<const __bf16*>(a.o) + qrow * D;
+#pragma unroll
+    for (int s = 0; s < C::NSTEP; ++s) {
+      const bf16x8_t ov = *reinterpret_cast<const bf16x8_t*>(op + 16 * s + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) delta = __builtin_fmaf((float)ov[e], (float)df[s][e], delta);
+    }
+  }
+  delta += __shfl_xor(delta, 32);
+  const float lse2 = valid ? a.lse[qrow] * kLog2e : __builtin_inff();
+  if (valid && g == 0) {
+    a.delta[qrow] = delta;
+    a.lse2[qrow] = lse2;
+  }
 
   // key ranges of the current pass (CHAIN: later passes put an ancestor
   // segment's range in r0, all of it at or before the item's first row)
@@ -1047,47 +1092,7 @@ void bwd_dkdv2_kernel(BwdArgs a, int first_item) {
   }  // items
 }
 
-// ------------------------------------------------------- pre and post passes
-// delta and lse2 for rows [T * Hq]: 16 lanes per row (8 elements each); the
-// accumulators are zeroed and the dK/dV item table is written (thread j:
-// item j of a kv head, j = 0 .. n_tab, the last entry being the first item
-// past the one-item launch) by the same grid
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a, int64_t nrows, int64_t nacc4) {
-  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gtid <= a.n_tab) {
-    const BwdItem bi = dkdv_item((int32_t)gtid, a.prefix_len, a.nseg, a.seg_offsets, a.seg_parent, a.row_chunk);
-    const int4 e = bi.valid ? int4{bi.k0, bi.k1, bi.r0, bi.r1} : int4{0, 0, 0, 0};
-    *reinterpret_cast<int4*>(a.item_tab + 4 * gtid) = e;
-  }
-  const int64_t row = gtid / (D / 8);
-  const int part = (int)(gtid % (D / 8));
-  float s = 0.f;
-  if (row < nrows) {
-    const u32x4_t o4 = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const __bf16*>(a.o) + row * D + 8 * part);
-    const u32x4_t d4 = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const __bf16*>(a.dout) + row * D + 8 * part);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float o0 = __builtin_bit_cast(float, o4[w] << 16), o1 = __builtin_bit_cast(float, o4[w] & 0xffff0000u);
-      const float d0 = __builtin_bit_cast(float, d4[w] << 16), d1 = __builtin_bit_cast(float, d4[w] & 0xffff0000u);
-      s = __builtin_fmaf(o0, d0, s);
-      s = __builtin_fmaf(o1, d1, s);
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < D / 8; m <<= 1) s += __shfl_xor(s, m);
-  if (row < nrows && part == 0) {
-    a.delta[row] = s;
-    a.lse2[row] = a.lse[row] * kLog2e;
-  }
-  const int64_t nthr = (int64_t)gridDim.x * 256;
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t i = gtid; i < nacc4; i += nthr) {
-    reinterpret_cast<f32x4_t*>(a.acc_k)[i] = z;
-    reinterpret_cast<f32x4_t*>(a.acc_v)[i] = z;
-  }
-}
-
+// ------------------------------------------------------------- post pass
 // dK = sm_scale acc_k, dV = acc_v, 8 elements per thread
 __global__ __launch_bounds__(256) void bwd_post_kernel(BwdArgs a, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1110,14 +1115,9 @@ constexpr int kBwdWalkPerHead = 4;
 
 template <int D>
 int launch_bwd_t(const BwdArgs& a, int64_t dq_blocks, int64_t dkdv_blocks, hipStream_t s) {
-  const int64_t nrows = a.total_tokens * a.hq;
-  const int64_t nacc4 = a.total_tokens * a.hkv * D / 4;
-  const int64_t pre_threads = nrows * (D / 8) > a.n_tab + 1 ? nrows * (D / 8) : a.n_tab + 1;
-  int64_t pre_blocks = (pre_threads + 255) / 256;
-  if (pre_blocks < 1) pre_blocks = 1;
-  hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, s, a, nrows, nacc4);
-  int err = (int)hipGetLastError();
-  if (err) return err;
+  int err = 0;
+  // the dQ launch also forms the row terms, zeroes the dK / dV accumulators
+  // and writes the item table (every flat layout with tokens has items)
   if (dq_blocks > 0) {
     if (a.seg_parent)
       hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)dq_blocks), dim3(kThreads), 0, s, a);
